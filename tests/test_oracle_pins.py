@@ -1,0 +1,517 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test fixes a part of the oracle by a closed form, a library routine, a
+finite difference, brute force or an invariant, chosen so that a plausible
+mistake (a dropped term, a wrong sign or index, a transposed operand) fails at
+least one of them.  Formulas cited are from:
+  [P1] "Training — design (ORPO, flash-CCE head, prefix sharing, segmented
+       backward)", §1 "The objective" and §5.1 "The head";
+  [P2] "ORPO training — design", "The objective", "File-by-file changes",
+       "Recommended defaults", "Parity".
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+from oracle import cce_oracle as O
+from linear_cross_entropy_forward_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers (test-side, independent evaluations)
+# ----------------------------------------------------------------------------
+def odds_ratio_log(lw, lr):
+    """Textbook log odds ratio: odds(p) = p / (1 - p) with p = e^l."""
+    pw, pr = math.exp(lw), math.exp(lr)
+    return math.log(pw / (1 - pw)) - math.log(pr / (1 - pr))
+
+
+def dec_log1mexp(x, digits=60):
+    """log(1 - e^x) in high-precision decimal arithmetic."""
+    getcontext().prec = digits
+    d = Decimal(repr(x))
+    return float((Decimal(1) - d.exp()).ln())
+
+
+def pair_rows(spans):
+    return WL.layout_pairs(spans)
+
+
+# ----------------------------------------------------------------------------
+# P1: closed-form ORPO scalars (hand-derived from [P1] §1 / [P2] "The objective")
+# ----------------------------------------------------------------------------
+E = math.e
+
+
+@pytest.mark.parametrize("lw,lr,lam,lo,lor,L,dlw,dlr", [
+    # (-1, -2): odds ratio = (e^2 - 1)/(e - 1) = e + 1, so log_odds = ln(1 + e);
+    # sigma(log_odds) = (1+e)/(2+e); d log_odds/d lw = e/(e-1), d/d lr = -e^2/(e^2-1).
+    (-1.0, -2.0, 0.1, math.log(1 + E), math.log((2 + E) / (1 + E)),
+     1.0 + 0.1 * math.log((2 + E) / (1 + E)),
+     -1.0 - 0.1 / (2 + E) * E / (E - 1), 0.1 / (2 + E) * E * E / (E * E - 1)),
+    # (-0.5, -0.5): log_odds = 0, L_OR = ln 2, sigma = 1/2.
+    (-0.5, -0.5, 0.1, 0.0, math.log(2.0), 0.5 + 0.1 * math.log(2.0),
+     -1.0 - 0.05 / (1 - math.exp(-0.5)), 0.05 / (1 - math.exp(-0.5))),
+])
+def test_p1_closed_form_scalars(lw, lr, lam, lo, lor, L, dlw, dlr):
+    assert O.log_odds(lw, lr) == pytest.approx(lo, rel=1e-13, abs=1e-14)
+    assert O.or_term(lw, lr) == pytest.approx(lor, rel=1e-13)
+    assert O.orpo_pair_loss(lw, lr, lam) == pytest.approx(L, rel=1e-13)
+    g = O.orpo_pair_grad(lw, lr, lam)
+    assert g[0] == pytest.approx(dlw, rel=1e-12)
+    assert g[1] == pytest.approx(dlr, rel=1e-12)
+
+
+def test_oracle_regression_fixture():
+    """The oracle's outputs on a tiny seeded case, written by
+    tests/golden/make_oracle_fixture.py (which calls only the oracle).  A
+    change here must come with the passage or reading that justifies it."""
+    with open(os.path.join(GOLDEN, "oracle_tiny_fixture.json")) as f:
+        fx = json.load(f)
+    H = np.array(fx["H"]); W = np.array(fx["W"])
+    y = np.array(fx["y"], np.int64); seg = np.array(fx["seg"], np.int64)
+    for sc, key in ((O.SCOPE_FULL, "full"), (O.SCOPE_RESPONSE, "response")):
+        out = O.step(H, W, y, seg, fx["n_pairs"], fx["lambda"], sc)
+        ref = fx[key]
+        for k in ("loss", "nll", "orv", "margin", "accuracy"):
+            assert out[k] == pytest.approx(ref[k], rel=1e-12, abs=1e-15)
+        for k in ("logp", "lse", "coef", "dh", "dW"):
+            np.testing.assert_allclose(out[k], np.array(ref[k]), rtol=1e-11, atol=1e-15)
+
+
+@pytest.mark.parametrize("lw,lr", [(-1.5, -0.7), (-11.2, -11.9), (-0.01, -3.0), (-25.0, -0.2)])
+def test_p1_log_odds_is_the_odds_ratio(lw, lr):
+    """log_odds equals the log of the ratio of odds p/(1-p) ([P1] §1)."""
+    assert O.log_odds(lw, lr) == pytest.approx(odds_ratio_log(lw, lr), rel=1e-9, abs=1e-12)
+
+
+def test_p1_mlx_lm_lora_variant_differs():
+    """The log_sigmoid(chosen - rejected) variant without the NLL term ([P1] §2)
+    is not our loss."""
+    for lw, lr in [(-1.0, -2.0), (-11.0, -12.0), (-3.0, -1.0)]:
+        ours = O.orpo_pair_loss(lw, lr, 0.1)
+        theirs = -math.log(1 / (1 + math.exp(-(lw - lr))))
+        assert abs(ours - theirs) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# P2: log1mexp stability ([P1] §1; [P2] "Recommended defaults": clamp / two-branch)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("x", [-math.log(2.0), -1.0, -20.0, -50.0, -1e-3, -0.3, -0.9, -700.0])
+def test_p2_log1mexp_matches_high_precision(x):
+    ref = dec_log1mexp(x)
+    got = O.log1mexp(x)
+    assert got == pytest.approx(ref, rel=1e-14, abs=1e-300)
+
+
+def test_p2_log1mexp_tail_not_zero():
+    # naive log(1 - exp(-50)) rounds to 0 in fp64; the two-branch form does not
+    assert O.log1mexp(-50.0) == pytest.approx(-1.9287498479639178e-22, rel=1e-12)
+    assert O.log1mexp(-800.0) == 0.0
+
+
+def test_p2_log1mexp_clamp():
+    clamp = math.log(1e-7)
+    assert O.log1mexp(-1e-10) == pytest.approx(clamp, rel=1e-15)
+    assert O.log1mexp(-1e-7) == pytest.approx(clamp, rel=1e-15)
+    assert O.dlog1mexp(-1e-10) == 0.0
+    # just outside the clamp the value is the exact one
+    x = -2e-7
+    assert O.log1mexp(x) == pytest.approx(dec_log1mexp(x), rel=1e-12)
+    # derivative: -e^x / (1 - e^x), checked by a central difference
+    for x in [-0.05, -1.0, -7.0]:
+        h = 1e-6
+        fd = (O.log1mexp(x + h) - O.log1mexp(x - h)) / (2 * h)
+        assert O.dlog1mexp(x) == pytest.approx(fd, rel=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# P3: full-scope NLL combine ([P1] §1)
+# ----------------------------------------------------------------------------
+def test_p3_full_nll_combine():
+    assert O.full_nll(-2.0, 3, -1.0, 2) == pytest.approx(1.6, rel=1e-15)
+    assert O.full_nll(-7.0, 0, -1.25, 9) == pytest.approx(1.25, rel=1e-15)
+    # in the batch epilogue: one pair, 3 prompt rows with logp -2, 2 chosen with -1
+    seg = pair_rows([(3, 2, 1)])
+    logp = np.array([-2, -2, -2, -1, -1, -0.5], float)
+    ep = O.epilogue(logp, seg, 1, 0.0, O.SCOPE_FULL)
+    assert ep["nll"] == pytest.approx(1.6, rel=1e-15)
+    assert ep["loss"] == pytest.approx(1.6, rel=1e-15)
+    ep = O.epilogue(logp, seg, 1, 0.0, O.SCOPE_RESPONSE)
+    assert ep["nll"] == pytest.approx(1.0, rel=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P4: library special case — lambda = 0, response scope: loss = mean CE over
+# the chosen rows; check forward against torch.nn.functional.cross_entropy and
+# the backward against torch.autograd (fp64, CPU).
+# ----------------------------------------------------------------------------
+def test_p4_torch_cross_entropy_and_autograd():
+    torch = pytest.importorskip("torch")
+    wl = WL.make_custom([(3, 9, 7, 2)], D=24, V=53, seed=11, hidden_scale=2.0, w_std=0.3)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    logp, lse = O.forward(H, W, y)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    Z = Ht @ Wt.T
+    valid = torch.tensor(y >= 0)
+    yt = torch.tensor(np.maximum(y, 0), dtype=torch.long)
+    ce = torch.nn.functional.cross_entropy(Z, yt, reduction="none")
+    np.testing.assert_allclose(logp[y >= 0], (-ce[valid]).detach().numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(Z, 1).detach().numpy(), rtol=1e-14)
+    assert np.all(logp[y < 0] == 0.0)
+
+    chosen = torch.tensor((seg & 3) == WL.KIND_CHOSEN)
+    loss_t = torch.nn.functional.cross_entropy(Z[chosen], yt[chosen], reduction="mean")
+    loss_t.backward()
+    ep = O.epilogue(logp, seg, 1, 0.0, O.SCOPE_RESPONSE)
+    assert ep["loss"] == pytest.approx(loss_t.item(), rel=1e-13)
+    dh, dW = O.backward(H, W, y, lse, ep["coef"])
+    np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_p4_autograd_full_orpo_chain():
+    """The analytic backward (coef from the epilogue, then G W / G^T H) equals
+    autograd through the plain composition logits -> log_softmax -> gather ->
+    per-pair means -> ORPO loss (torch fp64)."""
+    torch = pytest.importorskip("torch")
+    spans = [(4, 6, 5, 1), (0, 3, 4), (2, 5, 5, 3)]
+    wl = WL.make_custom(spans, D=16, V=29, seed=5, hidden_scale=1.5, w_std=0.4, lam=0.7)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    kind, pair = seg & 3, seg >> 2
+    for scope in (O.SCOPE_FULL, O.SCOPE_RESPONSE):
+        Ht = torch.tensor(H, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        lsm = torch.log_softmax(Ht @ Wt.T, dim=1)
+        lp = lsm[torch.arange(len(y)), torch.tensor(np.maximum(y, 0))] * torch.tensor(y >= 0)
+        losses = []
+        for b in range(len(spans)):
+            C = torch.tensor((pair == b) & (kind == WL.KIND_CHOSEN))
+            R = torch.tensor((pair == b) & (kind == WL.KIND_REJECTED))
+            Q = torch.tensor((pair == b) & (kind == WL.KIND_PROMPT))
+            lw, lr = lp[C].mean(), lp[R].mean()
+            lo = (lw - lr) - (torch.log(-torch.expm1(lw)) - torch.log(-torch.expm1(lr)))
+            orb = -torch.nn.functional.logsigmoid(lo)
+            if scope == O.SCOPE_FULL:
+                nll = -(lp[Q].sum() + lp[C].sum()) / (int(Q.sum()) + int(C.sum()))
+            else:
+                nll = -lw
+            losses.append((nll, orb))
+        nll = torch.stack([a for a, _ in losses]).mean()
+        orv = torch.stack([b for _, b in losses]).mean()
+        loss = nll + wl.lam * orv
+        loss.backward()
+        logp, lse = O.forward(H, W, y)
+        ep = O.epilogue(logp, seg, len(spans), wl.lam, scope)
+        assert ep["loss"] == pytest.approx(loss.item(), rel=1e-12)
+        assert ep["nll"] == pytest.approx(nll.item(), rel=1e-12)
+        assert ep["orv"] == pytest.approx(orv.item(), rel=1e-12)
+        dh, dW = O.backward(H, W, y, lse, ep["coef"])
+        np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
+        np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P5: closed form at W = 0
+# ----------------------------------------------------------------------------
+def test_p5_zero_head():
+    wl = WL.make_custom([(5, 7, 6, 2), (1, 4, 9)], D=12, V=37, seed=3)
+    H, y, seg = wl.h64(), wl.y, wl.seg
+    V = wl.V
+    W = np.zeros((V, wl.D))
+    logp, lse = O.forward(H, W, y)
+    assert np.all(lse == pytest.approx(math.log(V), rel=1e-15))
+    assert np.all(logp[y >= 0] == pytest.approx(-math.log(V), rel=1e-15))
+    ep = O.epilogue(logp, seg, 2, 0.3, O.SCOPE_FULL)
+    dh, dW = O.backward(H, W, y, lse, ep["coef"])
+    assert np.all(dh == 0.0)
+    coef = ep["coef"]
+    ref = np.zeros((V, wl.D))
+    for i in range(wl.M):
+        for v in range(V):
+            ref[v] += coef[i] * (1.0 / V - (1.0 if y[i] == v else 0.0)) * H[i]
+    np.testing.assert_allclose(dW, ref, rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P6: invariants
+# ----------------------------------------------------------------------------
+def _case():
+    spans = [(3, 8, 6, 2), (2, 5, 7)]
+    return WL.make_custom(spans, D=10, V=31, seed=9, hidden_scale=2.0, w_std=0.5, lam=0.4)
+
+
+def test_p6_invariants_forward():
+    wl = _case()
+    H, W, y = wl.h64(), wl.W64(), wl.y
+    logp, lse = O.forward(H, W, y)
+    Z = H @ W.T
+    assert np.all(logp <= 0.0)
+    assert np.all(lse >= Z.max(axis=1))
+    # vocab permutation
+    perm = np.random.default_rng(0).permutation(wl.V)
+    inv = np.argsort(perm)
+    y2 = np.where(y >= 0, inv[np.maximum(y, 0)], -1)
+    lp2, ls2 = O.forward(H, W[perm], y2)
+    np.testing.assert_allclose(lp2, logp, rtol=1e-13)
+    np.testing.assert_allclose(ls2, lse, rtol=1e-13)
+
+
+def test_p6_invariants_backward():
+    wl = _case()
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    logp, lse = O.forward(H, W, y)
+    ep = O.epilogue(logp, seg, wl.n_pairs, wl.lam, O.SCOPE_FULL)
+    coef = ep["coef"]
+    dh, dW = O.backward(H, W, y, lse, coef)
+    # sum over the vocab of dW is zero: each row's softmax sums to 1 = its onehot
+    np.testing.assert_allclose(dW.sum(axis=0), 0.0, atol=1e-12)
+    # per-row form of dh
+    P = np.exp(H @ W.T - lse[:, None])
+    for i in range(wl.M):
+        ref = coef[i] * (P[i] @ W - (W[y[i]] if y[i] >= 0 else 0.0))
+        np.testing.assert_allclose(dh[i], ref, rtol=1e-11, atol=1e-15)
+    # ignore rows: coef and dh rows exactly 0
+    ign = (seg & 3) == WL.KIND_IGNORE
+    assert np.all(coef[ign] == 0.0)
+    assert np.all(dh[ign] == 0.0)
+    # vocab permutation permutes dW
+    perm = np.random.default_rng(1).permutation(wl.V)
+    inv = np.argsort(perm)
+    y2 = np.where(y >= 0, inv[np.maximum(y, 0)], -1)
+    lp2, ls2 = O.forward(H, W[perm], y2)
+    ep2 = O.epilogue(lp2, seg, wl.n_pairs, wl.lam, O.SCOPE_FULL)
+    dh2, dW2 = O.backward(H, W[perm], y2, ls2, ep2["coef"])
+    np.testing.assert_allclose(dW2, dW[perm], rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dh2, dh, rtol=1e-10, atol=1e-14)
+
+
+def test_p6_invariants_epilogue():
+    rng = np.random.default_rng(4)
+    seg = WL.layout_pairs([(3, 5, 4, 1), (0, 6, 2)])
+    logp = -rng.uniform(0.5, 12, size=seg.shape[0])
+    for scope in (O.SCOPE_FULL, O.SCOPE_RESPONSE):
+        ep = O.epilogue(logp, seg, 2, 0.2, scope)
+        # row permutation within a pair's span leaves everything unchanged
+        perm = np.arange(len(seg))
+        perm[3:8] = perm[3:8][::-1]
+        ep2 = O.epilogue(logp[perm], seg[perm], 2, 0.2, scope)
+        assert ep2["loss"] == pytest.approx(ep["loss"], rel=1e-14)
+        # duplicating every pair leaves the batch means unchanged
+        seg_dup = np.concatenate([seg, seg + (2 << 2)])
+        ep3 = O.epilogue(np.concatenate([logp, logp]), seg_dup, 4, 0.2, scope)
+        for k in ("loss", "nll", "orv", "margin", "accuracy"):
+            assert ep3[k] == pytest.approx(ep[k], rel=1e-14)
+        # ignore rows carry no weight, and changing their logp changes nothing
+        ign = (seg & 3) == WL.KIND_IGNORE
+        assert np.all(ep["coef"][ign] == 0.0)
+        lp4 = logp.copy()
+        lp4[ign] = -99.0
+        assert O.epilogue(lp4, seg, 2, 0.2, scope)["loss"] == ep["loss"]
+        # prompt rows carry no weight in response scope
+        prm = (seg & 3) == WL.KIND_PROMPT
+        if scope == O.SCOPE_RESPONSE:
+            assert np.all(ep["coef"][prm] == 0.0)
+        else:
+            assert np.all(ep["coef"][prm] > 0.0)
+        # sign convention: chosen coef > 0, rejected coef < 0
+        assert np.all(ep["coef"][(seg & 3) == WL.KIND_CHOSEN] > 0)
+        assert np.all(ep["coef"][(seg & 3) == WL.KIND_REJECTED] < 0)
+
+
+def test_p6_accuracy_and_margin():
+    seg = WL.layout_pairs([(0, 1, 1), (0, 1, 1), (0, 1, 1)])
+    logp = np.array([-1.0, -2.0, -3.0, -3.0, -4.0, -1.0])
+    ep = O.epilogue(logp, seg, 3, 0.1, O.SCOPE_RESPONSE)
+    assert ep["accuracy"] == pytest.approx(1.0 / 3.0)       # strict >, tie is a miss
+    lo = [odds_ratio_log(-1, -2), 0.0, odds_ratio_log(-4, -1)]
+    assert ep["margin"] == pytest.approx(np.mean(lo), rel=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# P7: finite differences of the whole chain (H, W -> loss)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("scope", [O.SCOPE_FULL, O.SCOPE_RESPONSE])
+def test_p7_finite_differences(scope):
+    spans = [(2, 3, 2, 1), (1, 2, 3), (0, 1, 1)]          # M = 16, all four kinds
+    wl = WL.make_custom(spans, D=6, V=11, seed=21, hidden_scale=1.3, w_std=0.6, lam=0.35)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    B = len(spans)
+
+    def L(Hx, Wx):
+        lp, _ = O.forward(Hx, Wx, y)
+        return O.epilogue(lp, seg, B, wl.lam, scope)["loss"]
+
+    logp, lse = O.forward(H, W, y)
+    ep = O.epilogue(logp, seg, B, wl.lam, scope)
+    dh, dW = O.backward(H, W, y, lse, ep["coef"])
+    eps = 1e-6
+    fdH = np.zeros_like(H)
+    for i in range(H.shape[0]):
+        for d in range(H.shape[1]):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, d] += eps
+            Hm[i, d] -= eps
+            fdH[i, d] = (L(Hp, W) - L(Hm, W)) / (2 * eps)
+    fdW = np.zeros_like(W)
+    for v in range(W.shape[0]):
+        for d in range(W.shape[1]):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[v, d] += eps
+            Wm[v, d] -= eps
+            fdW[v, d] = (L(H, Wp) - L(H, Wm)) / (2 * eps)
+    assert np.linalg.norm(dh - fdH) / np.linalg.norm(fdH) < 1e-6
+    assert np.linalg.norm(dW - fdW) / np.linalg.norm(fdW) < 1e-6
+
+
+def test_p7_finite_differences_of_coef():
+    """coef_i = -dL/dlogp_i, by central differences on the epilogue alone."""
+    seg = WL.layout_pairs([(2, 3, 2, 1), (1, 2, 3)])
+    rng = np.random.default_rng(8)
+    logp = -rng.uniform(0.3, 4.0, size=seg.shape[0])
+    for scope in (O.SCOPE_FULL, O.SCOPE_RESPONSE):
+        ep = O.epilogue(logp, seg, 2, 0.6, scope)
+        for i in range(len(logp)):
+            e = 1e-6
+            lp, lm = logp.copy(), logp.copy()
+            lp[i] += e
+            lm[i] -= e
+            fd = (O.loss_from_logp(lp, seg, 2, 0.6, scope) - O.loss_from_logp(lm, seg, 2, 0.6, scope)) / (2 * e)
+            assert -fd == pytest.approx(ep["coef"][i], rel=1e-6, abs=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# P8: brute force with per-element loops (no matmul, no vector logsumexp)
+# ----------------------------------------------------------------------------
+def test_p8_brute_force():
+    spans = [(1, 2, 1, 1)]          # M = 5
+    wl = WL.make_custom(spans, D=3, V=7, seed=2, hidden_scale=1.0, w_std=0.8, lam=0.25)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    M, V, D = wl.M, wl.V, wl.D
+    z = [[sum(H[i][d] * W[v][d] for d in range(D)) for v in range(V)] for i in range(M)]
+    lse = [math.log(sum(math.exp(z[i][v]) for v in range(V))) for i in range(M)]
+    logp = [(z[i][y[i]] - lse[i]) if y[i] >= 0 else 0.0 for i in range(M)]
+    lp_o, lse_o = O.forward(H, W, y)
+    np.testing.assert_allclose(lp_o, logp, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse_o, lse, rtol=1e-12)
+    ep = O.epilogue(lp_o, seg, 1, wl.lam, O.SCOPE_FULL)
+    coef = ep["coef"]
+    dh = [[0.0] * D for _ in range(M)]
+    dW = [[0.0] * D for _ in range(V)]
+    for i in range(M):
+        for v in range(V):
+            g = coef[i] * (math.exp(z[i][v] - lse[i]) - (1.0 if v == y[i] else 0.0))
+            for d in range(D):
+                dh[i][d] += g * W[v][d]
+                dW[v][d] += g * H[i][d]
+    dh_o, dW_o = O.backward(H, W, y, lse_o, coef)
+    np.testing.assert_allclose(dh_o, dh, rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(dW_o, dW, rtol=1e-11, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P9: integer handling
+# ----------------------------------------------------------------------------
+def test_p9_counts_and_zero_coef():
+    spans = [(7, 11, 5, 3), (0, 2, 9, 4), (1, 1, 1)]
+    seg = WL.layout_pairs(spans)
+    logp = -np.linspace(1, 5, seg.shape[0])
+    ep = O.epilogue(logp, seg, 3, 0.1, O.SCOPE_RESPONSE)
+    assert list(ep["Pm1"]) == [7, 0, 1]
+    assert list(ep["Mw"]) == [11, 2, 1]
+    assert list(ep["Mr"]) == [5, 9, 1]
+    kind = seg & 3
+    assert np.all(ep["coef"][(kind == WL.KIND_IGNORE) | (kind == WL.KIND_PROMPT)] == 0.0)
+    with pytest.raises(ValueError):
+        O.epilogue(logp, WL.layout_pairs([(1, 3, 0, 0)] + spans[1:])[: len(logp)], 3, 0.1, O.SCOPE_FULL)
+
+
+def test_p9_target_gather_index():
+    """The gathered logit is z[i, y_i] exactly (not a neighbour, not transposed)."""
+    M, V, D = 6, 9, 4
+    H = np.eye(M, D) * 3.0
+    W = np.zeros((V, D))
+    for v in range(V):
+        W[v, v % D] = float(v)           # z[i, v] = 3 * v if v % D == i else 0
+    y = np.array([0, 5, 2, 7, -1, 3])
+    logp, lse = O.forward(H, W, y)
+    Z = H @ W.T
+    for i in range(M):
+        if y[i] >= 0:
+            assert logp[i] == Z[i, y[i]] - lse[i]
+
+
+# ----------------------------------------------------------------------------
+# filter mode (reported, not gated): it only drops sub-eps softmax entries
+# ----------------------------------------------------------------------------
+def test_filter_mode_drops_only_small_entries():
+    wl = WL.make_custom([(2, 6, 6)], D=8, V=200, seed=13, hidden_scale=3.0, w_std=1.0)
+    H, W, y = wl.h64(), wl.W64(), wl.y
+    logp, lse = O.forward(H, W, y)
+    coef = O.epilogue(logp, wl.seg, 1, 0.1, O.SCOPE_FULL)["coef"]
+    Z = H @ W.T
+    G0 = O.grad_logits(Z, lse, y, coef, 0.0)
+    G1 = O.grad_logits(Z, lse, y, coef, 1e-3)
+    P = np.exp(Z - lse[:, None])
+    changed = G0 != G1
+    assert np.all(P[changed] < 1e-3)
+    for i in range(wl.M):
+        assert G1[i, y[i]] == G0[i, y[i]]
+    assert changed.sum() > 0
+
+
+# ----------------------------------------------------------------------------
+# input generators
+# ----------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10 ** rng.uniform(-5, 5, 10000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -2.00390625, 0.0, -0.0], np.float32)])
+    ours = WL.f32_to_bf16_bits(x)
+    ref = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(WL.bf16_bits_to_f32(ours), torch.tensor(x).to(torch.bfloat16).float().numpy())
+
+
+def test_workload_determinism_and_layouts():
+    a = WL.make_workload("tiny")
+    b = WL.make_workload("tiny")
+    assert np.array_equal(a.h_bits, b.h_bits) and np.array_equal(a.W_bits, b.W_bits)
+    assert np.array_equal(a.y, b.y) and np.array_equal(a.seg, b.seg)
+    assert (a.M, a.D, a.V) == (287, 256, 4096)
+    kinds = np.bincount(a.seg & 3, minlength=4)
+    assert list(kinds) == [0, 31, 128, 128]
+    assert a.h_f32_raw is not None
+
+
+def test_stress_layout():
+    rng = np.random.default_rng(np.random.SeedSequence(WL.BASE_SEED + 4).spawn(4)[3])
+    spans = WL.stress_spans(rng)
+    seg = WL.layout_pairs(spans)
+    kinds = np.bincount(seg & 3, minlength=4)
+    assert seg.shape[0] == 16384
+    assert kinds[WL.KIND_IGNORE] == 1638 and kinds[WL.KIND_PROMPT] == 3277
+    assert kinds[WL.KIND_CHOSEN] + kinds[WL.KIND_REJECTED] == 11469
+    lens = [s[1] for s in spans] + [s[2] for s in spans]
+    assert min(lens) >= 64 and max(lens) <= 4096 and len(spans) == 8
+
+
+def test_zipf_histogram():
+    rng = np.random.default_rng(3)
+    V = 1000
+    ids = WL.zipf_ids(rng, 200000, V)
+    p = np.arange(1, V + 1, dtype=float) ** -1.1
+    p /= p.sum()
+    counts = np.bincount(ids, minlength=V)
+    for k in (0, 1, 2, 9, 99):
+        expect = p[k] * 200000
+        assert abs(counts[k] - expect) < 4.0 * math.sqrt(expect)     # 4 sigma
+    assert ids.min() >= 0 and ids.max() < V
