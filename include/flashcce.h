@@ -1,0 +1,151 @@
+/*
+ * flashcce.h — C-ABI of the flash-CCE ORPO head for MI355X (gfx950).
+ *
+ * The head computes, for hidden rows h[M,D] and a vocabulary head W[V,D]
+ * (both bf16, row-major, D contiguous) and targets y[M]:
+ *
+ *   logp_i = h_i . W_{y_i} - logsumexp_v (h_i . W_v)
+ *
+ * without ever storing the [M,V] logits ("Training — design (ORPO, flash-CCE
+ * head, prefix sharing, segmented backward)", §5.1 "The head"; "ORPO training
+ * — design", "Ranked levers", lever 1 and its "Implementation spec — fused
+ * linear-CE log-prob head": online max / sum-exp over vocab tiles, O(M) saved
+ * state), the ORPO objective on those log-probs (same pages, "The objective")
+ * and the head backward (dh, dW) from the saved per-row log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Array arguments are DEVICE pointers unless stated otherwise; scalars are
+ *    passed by value.  `stream` is a hipStream_t (NULL = the null stream).
+ *  - Every call only validates its arguments on the host and enqueues kernels
+ *    on `stream`; it returns before the GPU work completes.  Inputs must stay
+ *    alive and unmodified until that work has completed.  Nothing is
+ *    allocated: the caller owns every buffer, including the workspace.
+ *  - Host-detectable errors (NULL pointer, non-positive size, workspace too
+ *    small, bad enum, a current device that is not gfx950) return a status
+ *    immediately and enqueue nothing.  No exception crosses the ABI.
+ *  - Data errors found on the device are OR-ed into the caller's uint32
+ *    `dev_status` word as CCE_DERR_* bits; the library never clears it (the
+ *    caller zeroes it before the first call and reads it after a sync).
+ *  - Any M, V, D >= 1 is accepted; ragged tiles are masked inside the kernels.
+ *  - Results are deterministic: no floating-point atomics are used, so for
+ *    fixed inputs, shapes and eps the output bytes are identical run to run.
+ *  - Segment codes: seg_i = (pair << 2) | kind, kind one of CCE_KIND_*.
+ *    A row with y_i = -1 is ignored (logp 0, coef 0); such a row must have
+ *    kind CCE_KIND_IGNORE.
+ */
+#ifndef FLASHCCE_H
+#define FLASHCCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cce_status {
+  CCE_OK = 0,
+  CCE_EINVAL = 1,      /* NULL pointer, bad enum or non-finite scalar */
+  CCE_ESHAPE = 2,      /* M, V or D < 1, n_pairs < 1, or sizes too large */
+  CCE_EWORKSPACE = 3,  /* ws_bytes < cce_workspace_bytes(M, V, D) or ws misaligned */
+  CCE_EDEVICE = 4,     /* the current HIP device is not gfx950 */
+  CCE_ELAUNCH = 5      /* a kernel launch failed */
+} cce_status;
+
+enum { CCE_KIND_IGNORE = 0, CCE_KIND_PROMPT = 1, CCE_KIND_CHOSEN = 2, CCE_KIND_REJECTED = 3 };
+enum { CCE_SCOPE_FULL = 0, CCE_SCOPE_RESPONSE = 1 };
+
+/* Bits of the device status word. */
+enum {
+  CCE_DERR_TARGET = 1u,     /* y_i outside [-1, V), or y_i = -1 on a row that is not IGNORE */
+  CCE_DERR_PAIR = 2u,       /* a pair index >= n_pairs */
+  CCE_DERR_EMPTY_SPAN = 4u, /* a pair with no CHOSEN or no REJECTED row */
+  CCE_DERR_NONFINITE = 8u   /* a non-finite log-sum-exp or loss */
+};
+
+/* Version of this ABI (incremented on incompatible changes). */
+int cce_abi_version(void);
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* cce_status_string(int status);
+
+/*
+ * Workspace bytes needed by cce_forward, orpo_epilogue and cce_backward for
+ * these sizes (one workspace serves all three).  Host-only; no GPU call.
+ * It depends on M and D and is independent of V once V exceeds one backward
+ * vocab chunk (16384 entries): the backward walks the vocabulary in chunks of
+ * that fixed width.  Returns 0 for invalid sizes.
+ */
+size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D);
+
+/*
+ * Forward: per-row target log-prob and log-sum-exp.
+ *   "Training — design …" §5.1; "ORPO training — design", lever 1 spec.
+ *   h        [M, D] bf16 row-major (16-byte aligned rows are the fast path)
+ *   W        [V, D] bf16 row-major
+ *   y        [M] int32 target ids in [0, V), or -1 for an ignored row
+ *   logp     [M] fp32 out: z_{i,y_i} - lse_i, and 0 for rows with y_i = -1
+ *   lse      [M] fp32 out: logsumexp_v z_{i,v} (written for every row)
+ *   dev_status  uint32 (device) OR-ed with CCE_DERR_TARGET / _NONFINITE
+ *   ws, ws_bytes  device workspace of at least cce_workspace_bytes(M, V, D)
+ *                 bytes, 256-byte aligned; contents on entry are ignored.
+ */
+cce_status cce_forward(const void* h, const void* W, const int32_t* y,
+                       int64_t M, int64_t V, int64_t D,
+                       float* logp, float* lse, uint32_t* dev_status,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ORPO epilogue on the per-row log-probs.
+ *   "Training — design …" §1 "The objective"; "ORPO training — design",
+ *   "The objective" and "File-by-file changes" (loss.ts):
+ *     per pair b: lw = mean logp over CHOSEN rows, lr = mean over REJECTED,
+ *                 pm = mean over PROMPT rows (the P-1 prompt next-token rows);
+ *     log_odds_b = (lw - lr) - (log1mexp(lw) - log1mexp(lr)),
+ *       log1mexp(x) = log(1 - e^x), two-branch, clamped below at log(1e-7);
+ *     or_b  = softplus(-log_odds_b)  (= -log sigmoid(log_odds_b));
+ *     nll_b = -lw (RESPONSE scope) or -((P-1) pm + Mw lw) / ((P-1) + Mw) (FULL);
+ *     loss = mean_b nll_b + lambda * mean_b or_b.
+ *   logp     [M] fp32 (from cce_forward);  y [M] int32 (checked only);
+ *   seg      [M] int32 segment codes; n_pairs >= 1; scope CCE_SCOPE_*.
+ *   out5     [5] fp32 out: loss, nll, or, margin (= mean log_odds), accuracy
+ *            (= fraction of pairs with lw > lr).
+ *   pair_stats [n_pairs, 8] fp32 out (may be NULL): lw, lr, log_odds, nll_b,
+ *            or_b, and the span sizes Mw, Mr, P-1 (integers, exact in fp32).
+ *   coef     [M] fp32 out: -dloss/dlogp_i (positive on CHOSEN rows, negative on
+ *            REJECTED rows, 1/(B((P-1)+Mw)) on PROMPT rows in FULL scope, else 0).
+ *   dev_status OR-ed with CCE_DERR_PAIR / _EMPTY_SPAN / _TARGET / _NONFINITE.
+ *   Sums are accumulated in fp64 in a fixed order.
+ */
+cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg,
+                         int64_t M, int32_t n_pairs, float lambda, int scope,
+                         float* out5, float* pair_stats, float* coef,
+                         uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the head given the per-row coefficient coef_i = -dL/dlogp_i:
+ *   G_{i,v} = coef_i (softmax_{i,v} - [v = y_i]),  dh = G W,  dW = G^T h.
+ *   "Training — design …" §5.1 (analytic backward from the saved LSE;
+ *   backward skips); "ORPO training — design", lever 1 spec (backward).
+ *   h, W, y  as for cce_forward;  lse [M], coef [M] fp32.
+ *   filter_eps  >= 0; softmax entries below it are dropped (never the target's).
+ *   block_eps   >= 0; a 256x256 (row, vocab) tile whose largest softmax entry
+ *               is below it and that holds no row's target is skipped.
+ *               0 and 0 give the exact gradient.
+ *   dh [M, D] fp32 out (overwritten); dW [V, D] fp32 out (overwritten).
+ *   G is rounded to bf16 (round-to-nearest-even) before the two contractions;
+ *   accumulation is fp32.
+ */
+cce_status cce_backward(const void* h, const void* W, const int32_t* y,
+                        const float* lse, const float* coef,
+                        int64_t M, int64_t V, int64_t D,
+                        float filter_eps, float block_eps,
+                        float* dh, float* dW, uint32_t* dev_status,
+                        void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHCCE_H */

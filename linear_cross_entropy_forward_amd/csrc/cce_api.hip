@@ -1,0 +1,226 @@
+// C-ABI entry points of the flash-CCE head (declared in include/flashcce.h).
+//
+// Each entry point validates its arguments on the host (before any HIP call,
+// so argument errors can be checked without a GPU), checks that the current
+// device is gfx950, carves the caller's workspace, and enqueues its kernels on
+// the caller's stream.  Nothing is allocated here.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/flashcce.h"
+#include "cce_launch.hpp"
+
+namespace {
+
+using cce::kTile;
+using cce::kVocabChunk;
+
+constexpr int64_t kMaxM = int64_t(1) << 21;  // keeps 256 * Mpad * 2 bytes < 2^31
+constexpr int64_t kMaxV = int64_t(1) << 30;
+constexpr int64_t kMaxD = 65536;
+constexpr size_t kAlign = 256;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool sizes_ok(int64_t M, int64_t V, int64_t D) {
+  return M >= 1 && V >= 1 && D >= 1 && M <= kMaxM && V <= kMaxV && D <= kMaxD;
+}
+
+// Forward vocab split: T tiles per workgroup so that nMt * S workgroups cover
+// the vocabulary in about one round of 256 workgroups (one per CU).
+void fwd_split(int64_t nMt, int64_t nVt, int& S, int& T) {
+  const int64_t tiles = nMt * nVt;
+  int64_t t = (tiles + 255) / 256;
+  if (t < 1) t = 1;
+  T = (int)t;
+  S = (int)((nVt + t - 1) / t);
+}
+// Upper bound of S over all V for this M (so the workspace does not grow with V).
+int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 1; }
+
+struct Layout {
+  int64_t Mpad, Dpad, Vc, nMt;
+  size_t part_m, part_s, tgt, pairs, ht, wt, g, gt, flags, total;
+};
+
+Layout layout(int64_t M, int64_t V, int64_t D) {
+  Layout L{};
+  L.nMt = (M + kTile - 1) / kTile;
+  L.Mpad = L.nMt * kTile;
+  L.Dpad = round_up(D, kTile);
+  L.Vc = round_up(V, kTile) < kVocabChunk ? round_up(V, kTile) : kVocabChunk;
+  const int64_t Scap = fwd_split_cap(L.nMt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.part_m = take((size_t)Scap * L.Mpad * sizeof(float));
+  L.part_s = take((size_t)Scap * L.Mpad * sizeof(float));
+  L.tgt = take((size_t)L.Mpad * sizeof(float));
+  L.pairs = take((size_t)L.Mpad * cce::kPairStride * sizeof(double));
+  L.ht = take((size_t)L.Dpad * L.Mpad * 2);
+  L.wt = take((size_t)L.Dpad * L.Vc * 2);
+  L.g = take((size_t)L.Mpad * L.Vc * 2);
+  L.gt = take((size_t)L.Vc * L.Mpad * 2);
+  L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
+  L.total = off;
+  return L;
+}
+
+// gfx950 check of the current device, cached per device id.
+cce_status device_ok() {
+  static std::mutex mu;
+  static int cache[64];  // 0 unknown, 1 ok, 2 not ok
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CCE_EDEVICE;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> g(mu);
+    if (cache[dev] == 1) return CCE_OK;
+    if (cache[dev] == 2) return CCE_EDEVICE;
+  }
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CCE_EDEVICE;
+  const bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> g(mu);
+    cache[dev] = ok ? 1 : 2;
+  }
+  return ok ? CCE_OK : CCE_EDEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int cce_abi_version(void) { return 1; }
+
+const char* cce_status_string(int status) {
+  switch (status) {
+    case CCE_OK: return "CCE_OK";
+    case CCE_EINVAL: return "CCE_EINVAL: invalid argument (null pointer, bad enum or non-finite scalar)";
+    case CCE_ESHAPE: return "CCE_ESHAPE: invalid sizes";
+    case CCE_EWORKSPACE: return "CCE_EWORKSPACE: workspace too small or misaligned";
+    case CCE_EDEVICE: return "CCE_EDEVICE: current device is not gfx950";
+    case CCE_ELAUNCH: return "CCE_ELAUNCH: kernel launch failed";
+    default: return "unknown cce_status";
+  }
+}
+
+size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D) {
+  if (!sizes_ok(M, V, D)) return 0;
+  return layout(M, V, D).total;
+}
+
+cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M, int64_t V,
+                       int64_t D, float* logp, float* lse, uint32_t* dev_status, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!h || !W || !y || !logp || !lse || !dev_status || !ws) return CCE_EINVAL;
+  if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
+  const Layout L = layout(M, V, D);
+  if (ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return CCE_EWORKSPACE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  char* base = static_cast<char*>(ws);
+  cce::FwdArgs a{};
+  a.H = static_cast<const cce::u16*>(h);
+  a.W = static_cast<const cce::u16*>(W);
+  a.y = y;
+  a.M = (int)M;
+  a.V = (int)V;
+  a.D = (int)D;
+  a.nMt = (int)L.nMt;
+  a.nVt = (int)((V + kTile - 1) / kTile);
+  fwd_split(a.nMt, a.nVt, a.S, a.T);
+  a.Mpad = (int)L.Mpad;
+  a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
+  a.part_m = reinterpret_cast<float*>(base + L.part_m);
+  a.part_s = reinterpret_cast<float*>(base + L.part_s);
+  a.tgt = reinterpret_cast<float*>(base + L.tgt);
+  a.logp = logp;
+  a.lse = lse;
+  a.status = dev_status;
+  return cce::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
+                                                                               : CCE_ELAUNCH;
+}
+
+cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg, int64_t M,
+                         int32_t n_pairs, float lambda, int scope, float* out5, float* pair_stats,
+                         float* coef, uint32_t* dev_status, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!logp || !y || !seg || !out5 || !coef || !dev_status || !ws) return CCE_EINVAL;
+  if (scope != CCE_SCOPE_FULL && scope != CCE_SCOPE_RESPONSE) return CCE_EINVAL;
+  if (!isfinite(lambda)) return CCE_EINVAL;
+  if (M < 1 || M > kMaxM || n_pairs < 1 || (int64_t)n_pairs > M) return CCE_ESHAPE;
+  // the epilogue's part of the workspace depends on M only; any V, D >= 1 give it
+  const Layout L = layout(M, 1, 1);
+  if (ws_bytes < L.pairs + (size_t)L.Mpad * cce::kPairStride * sizeof(double) ||
+      (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return CCE_EWORKSPACE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  cce::EpiArgs a{};
+  a.logp = logp;
+  a.y = y;
+  a.seg = seg;
+  a.M = (int)M;
+  a.n_pairs = n_pairs;
+  a.lambda = (double)lambda;
+  a.scope = scope;
+  a.pairs = reinterpret_cast<double*>(static_cast<char*>(ws) + L.pairs);
+  a.out5 = out5;
+  a.pair_stats = pair_stats;
+  a.coef = coef;
+  a.status = dev_status;
+  return cce::launch_epilogue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
+                                                                                : CCE_ELAUNCH;
+}
+
+cce_status cce_backward(const void* h, const void* W, const int32_t* y, const float* lse,
+                        const float* coef, int64_t M, int64_t V, int64_t D, float filter_eps,
+                        float block_eps, float* dh, float* dW, uint32_t* dev_status, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!h || !W || !y || !lse || !coef || !dh || !dW || !dev_status || !ws) return CCE_EINVAL;
+  if (!(filter_eps >= 0.f) || !(block_eps >= 0.f) || !isfinite(filter_eps) || !isfinite(block_eps))
+    return CCE_EINVAL;
+  if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
+  const Layout L = layout(M, V, D);
+  if (ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return CCE_EWORKSPACE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  char* base = static_cast<char*>(ws);
+  cce::BwdArgs a{};
+  a.H = static_cast<const cce::u16*>(h);
+  a.W = static_cast<const cce::u16*>(W);
+  a.y = y;
+  a.lse = lse;
+  a.coef = coef;
+  a.M = (int)M;
+  a.V = (int)V;
+  a.D = (int)D;
+  a.nMt = (int)L.nMt;
+  a.Mpad = (int)L.Mpad;
+  a.Dpad = (int)L.Dpad;
+  a.Vc = (int)L.Vc;
+  a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
+  a.filter_eps = filter_eps;
+  a.block_eps = block_eps;
+  a.dh = dh;
+  a.dW = dW;
+  a.HT = reinterpret_cast<cce::u16*>(base + L.ht);
+  a.WT = reinterpret_cast<cce::u16*>(base + L.wt);
+  a.G = reinterpret_cast<cce::u16*>(base + L.g);
+  a.GT = reinterpret_cast<cce::u16*>(base + L.gt);
+  a.flags = reinterpret_cast<int*>(base + L.flags);
+  a.status = dev_status;
+  return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
+                                                                                : CCE_ELAUNCH;
+}
+
+}  // extern "C"

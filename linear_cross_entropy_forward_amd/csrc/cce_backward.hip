@@ -1,0 +1,266 @@
+// Backward of the flash-CCE head.
+//
+// "Training — design (ORPO, flash-CCE head, …)" §5.1 (the analytic backward
+// recomputes the logits from the saved per-row LSE and forms
+// g (onehot - softmax); backward skips of near-zero softmax) and "ORPO training
+// — design", lever 1 spec (backward).  With coef = -dL/dlogp:
+//   G[i, v] = coef_i (softmax(i, v) - [v = y_i]),  dh = G W,  dW = G^T h.
+//
+// The vocabulary is walked in chunks of kVocabChunk entries.  Per chunk:
+//   1. WT = W[chunk]^T             (bf16, zero padded)       HBM-bound
+//   2. recompute z = h W[chunk]^T, G = coef (softmax - onehot), optional
+//      filter / tile skip; G and G^T written as bf16 (RNE)   MFMA
+//   3. dW[chunk] = G^T h           (A = G^T, B = h^T)        MFMA
+//   4. dh (+)= G W[chunk]          (A = G,   B = WT)         MFMA
+// Every contraction is the same NT GEMM core with K contiguous in both
+// operands; h^T is formed once per call.  dh accumulates across chunks in
+// stream order, so no atomics are used and results are deterministic.  The
+// workspace (G, G^T, WT, h^T) depends on M and D but not on V.
+#include "cce_device.hpp"
+#include "cce_launch.hpp"
+
+namespace cce {
+
+// dst[c][r] = src[r][c] for r < R, c < C, and 0 elsewhere in the
+// [dst_rows, dst_cols] destination (pitch ld_dst).  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ src, int R, int C,
+                                                   int ld_src, u16* __restrict__ dst, int dst_rows,
+                                                   int dst_cols, int ld_dst, int vec) {
+  __shared__ u16 t[64][66];
+  const int r0 = blockIdx.x * 64;  // source rows = destination columns
+  const int c0 = blockIdx.y * 64;  // source columns = destination rows
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + 256 * p;  // 512 chunks of 8 elements
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    u16 e[8];
+    if (vec && r < R && c + 8 <= C) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_src + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        e[2 * k] = (u16)(v[k] & 0xffffu);
+        e[2 * k + 1] = (u16)(v[k] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = (r < R && c + k < C) ? src[(size_t)r * ld_src + c + k] : (u16)0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[rr][cc + k] = e[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + 256 * p;
+    const int dr = q >> 3, dc = (q & 7) * 8;  // destination row (source column), column block
+    const int orow = c0 + dr, ocol = r0 + dc;
+    if (orow >= dst_rows || ocol >= dst_cols) continue;
+    unsigned w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (unsigned)t[dc + 2 * k][dr] | ((unsigned)t[dc + 2 * k + 1][dr] << 16);
+    *reinterpret_cast<u32x4*>(dst + (size_t)orow * ld_dst + ocol) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Recompute one 256 (vocab) x 256 (token) logit tile of the chunk and write its
+// gradient tile.  A = W rows of the chunk, B = h rows, so each lane owns one
+// token (lse, coef, target in registers) and 16 vocab entries per MFMA tile.
+template <bool VEC, bool FILTER>
+__global__ __launch_bounds__(NT, 1) void k_recompute(
+    const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
+    const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
+    int vlen, int nMt, int nvt, int nlaunch, float filter_eps, float block_eps,
+    u16* __restrict__ G, u16* __restrict__ GT, int* __restrict__ flags, int Mpad, int Vc) {
+  __shared__ Smem sm;
+  __shared__ float red[4];
+  int mt, vt;
+  if (!map_tile(blockIdx.x, nlaunch, nMt, nvt, 8, mt, vt)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+
+  floatx16 acc[4][4];
+  gemm_tile<VEC, false>(Wc + (size_t)vt * TILE * D, D, min(TILE, vlen - vt * TILE),
+                        H + (size_t)mt * TILE * D, D, min(TILE, M - mt * TILE), D, nullptr, 0, sm,
+                        acc);
+
+  const int vl0 = vt * TILE + wi * 128;  // chunk-local vocab row of this wave's first A row
+  float nlse[4], cf[4];
+  int off[4];
+  bool any_tgt_lane = false;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
+    const bool ok = j < M;
+    nlse[jj] = ok ? -lse[j] * LOG2E : 0.f;
+    cf[jj] = ok ? coef[j] : 0.f;
+    const int yy = ok ? y[j] : -1;
+    off[jj] = (yy >= 0) ? yy - (v0 + vl0) - 4 * half : -1000000;
+    const int o = (yy >= 0) ? yy - (v0 + vl0) : -1;
+    any_tgt_lane |= (unsigned)o < 128u;
+  }
+  // softmax entries into acc; rows beyond the chunk's valid vocab become 0
+  const bool vtail = vt * TILE + TILE > vlen;
+  float pmax = 0.f;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool vbad = vtail && (vl0 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= vlen);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float p = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nlse[jj]));
+        if (vbad) p = 0.f;
+        acc[ii][jj][r] = p;
+        pmax = fmaxf(pmax, p);
+      }
+    }
+  int* flag = flags + (size_t)mt * (Vc / TILE) + vt;
+  if (block_eps > 0.f) {
+    // skip the tile if every softmax entry is below block_eps and no token of
+    // the tile has its target among the tile's vocab rows
+    const bool keep_lane = pmax >= block_eps || any_tgt_lane;
+    const bool keep_wave = __ballot(keep_lane) != 0ull;
+    if (lane == 0) red[w] = keep_wave ? 1.f : 0.f;
+    __syncthreads();
+    const bool keep = (red[0] + red[1] + red[2] + red[3]) > 0.f;
+    if (!keep) {
+      if (tid == 0) *flag = 0;
+      return;
+    }
+  }
+  if (tid == 0) *flag = 1;
+
+  const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
+    u16* gt_col = GT + j;
+    u16* g_row = G + (size_t)j * Vc;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e;
+          float p = acc[ii][jj][r];
+          const bool is_t = wave_has_tgt && (off[jj] == ii * 32 + 8 * q + e);
+          if (FILTER && p < filter_eps && !is_t) p = 0.f;
+          g[e] = cf[jj] * (is_t ? p - 1.f : p);
+        }
+        const int vl = vl0 + ii * 32 + 8 * q + 4 * half;
+        u32x2 pk = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+        *reinterpret_cast<u32x2*>(g_row + vl) = pk;
+        gt_col[(size_t)(vl + 0) * Mpad] = (u16)(pk[0] & 0xffffu);
+        gt_col[(size_t)(vl + 1) * Mpad] = (u16)(pk[0] >> 16);
+        gt_col[(size_t)(vl + 2) * Mpad] = (u16)(pk[1] & 0xffffu);
+        gt_col[(size_t)(vl + 3) * Mpad] = (u16)(pk[1] >> 16);
+      }
+    }
+  }
+}
+
+// C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k] with fp32 output.
+// kflags: per 256-wide K block of A-tile ta, flags[ta*fa + kb*fk] (null = all).
+template <bool ACCUM, bool SKIP>
+__global__ __launch_bounds__(NT, 1) void k_gemm_f32out(
+    const u16* __restrict__ A, int lda, int a_rows, const u16* __restrict__ B, int ldb, int b_rows,
+    int K, float* __restrict__ C, int ldc, int c_rows, int c_cols, int nA, int nB, int nlaunch,
+    const int* __restrict__ kflags, int fa, int fk) {
+  __shared__ Smem sm;
+  int ta, tb;
+  if (!map_tile(blockIdx.x, nlaunch, nA, nB, 8, ta, tb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+  floatx16 acc[4][4];
+  gemm_tile<true, SKIP>(A + (size_t)ta * TILE * lda, lda, min(TILE, a_rows - ta * TILE),
+                        B + (size_t)tb * TILE * ldb, ldb, min(TILE, b_rows - tb * TILE), K,
+                        SKIP ? kflags + (size_t)ta * fa : nullptr, fk, sm, acc);
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = ta * TILE + wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (row >= c_rows) continue;
+      float* crow = C + (size_t)row * ldc;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = tb * TILE + wj * 128 + jj * 32 + (lane & 31);
+        if (col < c_cols) {
+          if (ACCUM) crow[col] += acc[ii][jj][r];
+          else crow[col] = acc[ii][jj][r];
+        }
+      }
+    }
+}
+
+static inline int pad8(int n) { return (n + 7) / 8 * 8; }
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
+  hipError_t e;
+  const int nDt = a.Dpad / kTile;
+  // h^T [Dpad, Mpad], zero padded
+  hipLaunchKernelGGL(k_transpose, dim3(a.Mpad / 64, a.Dpad / 64), dim3(256), 0, st, a.H, a.M, a.D,
+                     a.D, a.HT, a.Dpad, a.Mpad, a.Mpad, (int)a.vec);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool filt = a.filter_eps > 0.f;
+  for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
+    const int vlen = a.V - v0 < a.Vc ? a.V - v0 : a.Vc;
+    const int nvt = (vlen + kTile - 1) / kTile;
+    const u16* Wc = a.W + (size_t)v0 * a.D;
+    // 1. WT = W[chunk]^T, [Dpad, nvt*256] used of [Dpad, Vc]
+    hipLaunchKernelGGL(k_transpose, dim3(nvt * kTile / 64, a.Dpad / 64), dim3(256), 0, st, Wc, vlen,
+                       a.D, a.D, a.WT, a.Dpad, nvt * kTile, a.Vc, (int)a.vec);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 2. recompute + gradient tile
+    {
+      const int n = a.nMt * nvt, nl = pad8(n);
+#define CCE_RECOMPUTE(VEC, FILT)                                                                   \
+  hipLaunchKernelGGL((k_recompute<VEC, FILT>), dim3(nl), dim3(NT), 0, st, a.H, Wc, a.y, a.lse,     \
+                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, nl, a.filter_eps, a.block_eps, a.G,   \
+                     a.GT, a.flags, a.Mpad, a.Vc)
+      if (a.vec) {
+        if (filt) CCE_RECOMPUTE(true, true); else CCE_RECOMPUTE(true, false);
+      } else {
+        if (filt) CCE_RECOMPUTE(false, true); else CCE_RECOMPUTE(false, false);
+      }
+#undef CCE_RECOMPUTE
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const bool skip = a.block_eps > 0.f;
+    const int fstride = a.Vc / kTile;
+    // 3. dW[chunk] = G^T h : A = GT [nvt*256 rows, K = Mpad], B = HT [Dpad rows, K = Mpad]
+    {
+      const int n = nvt * nDt, nl = pad8(n);
+#define CCE_DW(SKIP)                                                                               \
+  hipLaunchKernelGGL((k_gemm_f32out<false, SKIP>), dim3(nl), dim3(NT), 0, st, a.GT, a.Mpad,         \
+                     nvt * kTile, a.HT, a.Mpad, a.Dpad, a.Mpad, a.dW + (size_t)v0 * a.D, a.D, vlen, \
+                     a.D, nvt, nDt, nl, a.flags, 1, fstride)
+      if (skip) CCE_DW(true); else CCE_DW(false);
+#undef CCE_DW
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // 4. dh (+)= G W[chunk] : A = G [Mpad rows, K = nvt*256], B = WT [Dpad rows, K = nvt*256]
+    {
+      const int n = a.nMt * nDt, nl = pad8(n);
+#define CCE_DH(ACC, SKIP)                                                                          \
+  hipLaunchKernelGGL((k_gemm_f32out<ACC, SKIP>), dim3(nl), dim3(NT), 0, st, a.G, a.Vc, a.Mpad,      \
+                     a.WT, a.Vc, a.Dpad, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, nl, a.flags, \
+                     fstride, 1)
+      if (v0 == 0) {
+        if (skip) CCE_DH(false, true); else CCE_DH(false, false);
+      } else {
+        if (skip) CCE_DH(true, true); else CCE_DH(true, false);
+      }
+#undef CCE_DH
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace cce

@@ -1,0 +1,137 @@
+"""Host-side checks of the C-ABI library (no kernel is launched here).
+
+The library must load, export every function include/flashcce.h declares, size
+its workspace independently of V, and reject bad arguments on the host before
+touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_forward_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashcce.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH),
+                                reason="libflashcce.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == {"cce_abi_version", "cce_status_string", "cce_workspace_bytes", "cce_forward",
+                     "orpo_epilogue", "cce_backward"}
+    assert names == set(B.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert B.load().cce_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert B.status_string(s).startswith("CCE_")
+    assert "unknown" in B.status_string(99)
+
+
+def test_workspace_is_independent_of_V():
+    M, D = 8192, 2560
+    sizes = [B.workspace_bytes(M, V, D) for V in (32768, 65536, 131072, 262144, 1 << 20)]
+    assert len(set(sizes)) == 1 and sizes[0] > 0
+    # and it does not grow with V below one chunk either beyond the chunk size
+    assert B.workspace_bytes(M, 300, D) <= sizes[0]
+    assert B.workspace_bytes(0, 10, 10) == 0
+    assert B.workspace_bytes(10, 0, 10) == 0
+    assert B.workspace_bytes(10, 10, 0) == 0
+    assert B.workspace_bytes(1 << 22, 10, 10) == 0
+
+
+def test_workspace_bound_at_gemma_and_stress():
+    # bf16 gradient chunk and its transpose dominate: 4 * Mpad * 16384 bytes
+    gemma = B.workspace_bytes(8192, 262144, 2560)
+    stress = B.workspace_bytes(16384, 262144, 4096)
+    assert gemma < 0.75e9
+    assert stress < 1.5e9
+
+
+FAKE = 1 << 20   # a non-null pointer value; never dereferenced on these paths
+
+
+def test_forward_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes(300, 1000, 64)
+    ok = (FAKE, FAKE, FAKE, 300, 1000, 64, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    for i in (0, 1, 2, 6, 7, 8, 9):
+        args = list(ok)
+        args[i] = None
+        assert lib.cce_forward(*args) == B.CCE_EINVAL
+    for i in (3, 4, 5):
+        args = list(ok)
+        args[i] = 0
+        assert lib.cce_forward(*args) == B.CCE_ESHAPE
+    args = list(ok)
+    args[10] = ws - 1
+    assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
+    args = list(ok)
+    args[9] = FAKE * 256 + 16          # misaligned workspace
+    assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
+
+
+def test_epilogue_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes(300, 1, 1)
+    ok = [FAKE, FAKE, FAKE, 300, 2, 0.1, 0, FAKE, None, FAKE, FAKE, FAKE * 256, ws, None]
+    a = list(ok); a[6] = 7
+    assert lib.orpo_epilogue(*a) == B.CCE_EINVAL
+    a = list(ok); a[5] = float("nan")
+    assert lib.orpo_epilogue(*a) == B.CCE_EINVAL
+    a = list(ok); a[4] = 0
+    assert lib.orpo_epilogue(*a) == B.CCE_ESHAPE
+    a = list(ok); a[4] = 301
+    assert lib.orpo_epilogue(*a) == B.CCE_ESHAPE
+    a = list(ok); a[0] = None
+    assert lib.orpo_epilogue(*a) == B.CCE_EINVAL
+    a = list(ok); a[12] = 10
+    assert lib.orpo_epilogue(*a) == B.CCE_EWORKSPACE
+
+
+def test_backward_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes(300, 1000, 64)
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None]
+    a = list(ok); a[8] = -1.0
+    assert lib.cce_backward(*a) == B.CCE_EINVAL
+    a = list(ok); a[9] = float("inf")
+    assert lib.cce_backward(*a) == B.CCE_EINVAL
+    a = list(ok); a[11] = None
+    assert lib.cce_backward(*a) == B.CCE_EINVAL
+    a = list(ok); a[7] = -3
+    assert lib.cce_backward(*a) == B.CCE_ESHAPE
+    a = list(ok); a[14] = 1
+    assert lib.cce_backward(*a) == B.CCE_EWORKSPACE
+
+
+def test_valid_call_without_gfx950_is_refused():
+    """With valid arguments and no gfx950 device the library refuses (it never
+    falls back to another path)."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is visible; covered by the gpu tests")
+    except Exception:
+        pass
+    lib = B.load()
+    ws = B.workspace_bytes(300, 1000, 64)
+    st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    assert st == B.CCE_EDEVICE
