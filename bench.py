@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--filter-eps", type=float, default=None,
                     help="coefficient filter eps (default: the workload's own setting)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
     return ap.parse_args()
 

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ src, 
 // Recompute one 256 (vocab) x 256 (token) logit tile of the chunk and write its
 // gradient tile.  A = W rows of the chunk, B = h rows, so each lane owns one
 // token (lse, coef, target in registers) and 16 vocab entries per MFMA tile.
-template <bool VEC, bool FILTER>
+template <bool VEC, bool FILTER, bool KTAIL>
 __global__ __launch_bounds__(NT, 1) void k_recompute(
     const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
     const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
 
   floatx16 acc[4][4];
-  gemm_tile<VEC, false>(Wc + (size_t)vt * TILE * D, D, min(TILE, vlen - vt * TILE),
+  gemm_tile<VEC, false, KTAIL>(Wc + (size_t)vt * TILE * D, D, min(TILE, vlen - vt * TILE),
                         H + (size_t)mt * TILE * D, D, min(TILE, M - mt * TILE), D, nullptr, 0, sm,
                         acc);
 
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm_f32out(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   floatx16 acc[4][4];
-  gemm_tile<true, SKIP>(A + (size_t)ta * TILE * lda, lda, min(TILE, a_rows - ta * TILE),
+  gemm_tile<true, SKIP, false>(A + (size_t)ta * TILE * lda, lda, min(TILE, a_rows - ta * TILE),
                         B + (size_t)tb * TILE * ldb, ldb, min(TILE, b_rows - tb * TILE), K,
                         SKIP ? kflags + (size_t)ta * fa : nullptr, fk, sm, acc);
 #pragma unroll
@@ -219,14 +219,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     // 2. recompute + gradient tile
     {
       const int n = a.nMt * nvt, nl = pad8(n);
-#define CCE_RECOMPUTE(VEC, FILT)                                                                   \
-  hipLaunchKernelGGL((k_recompute<VEC, FILT>), dim3(nl), dim3(NT), 0, st, a.H, Wc, a.y, a.lse,     \
+#define CCE_RECOMPUTE(VEC, FILT, KT)                                                               \
+  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT>), dim3(nl), dim3(NT), 0, st, a.H, Wc, a.y, a.lse, \
                      a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, nl, a.filter_eps, a.block_eps, a.G,   \
                      a.GT, a.flags, a.Mpad, a.Vc)
-      if (a.vec) {
-        if (filt) CCE_RECOMPUTE(true, true); else CCE_RECOMPUTE(true, false);
+      const bool kt = a.D % BK != 0;
+      if (!a.vec) {
+        if (filt) CCE_RECOMPUTE(false, true, false); else CCE_RECOMPUTE(false, false, false);
+      } else if (kt) {
+        if (filt) CCE_RECOMPUTE(true, true, true); else CCE_RECOMPUTE(true, false, true);
       } else {
-        if (filt) CCE_RECOMPUTE(false, true); else CCE_RECOMPUTE(false, false);
+        if (filt) CCE_RECOMPUTE(true, true, false); else CCE_RECOMPUTE(true, false, false);
       }
 #undef CCE_RECOMPUTE
       if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -112,7 +112,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                            0x00020000);
 }
 
-template <bool VEC>
+template <bool VEC, bool KTAIL>
 struct SliceLoader {
   const u16* base;
   int ld;
@@ -135,18 +135,17 @@ struct SliceLoader {
     }
   }
 
+  // Issues the loads of K-slice k0 (one global load per row this thread moves).
   __device__ __forceinline__ void load(int k0, int tid) {
     if (VEC) {
       // the whole offset rides in the VGPR offset (always range-checked);
-      // the scalar offset stays 0
+      // the scalar offset stays 0.  A chunk at k >= K (K tail, K % 8 == 0) is
+      // pointed past the resource so that it reads as zero.
+      const bool kv = !KTAIL || k0 + (tid & 7) * 8 < K;
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        r[p] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + p * rstride + k0 * 2, 0, 0);
-      if (k0 + BK > K) {  // K tail: zero the chunks at k >= K (uniform branch)
-        const bool kv = k0 + (tid & 7) * 8 < K;
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-          if (!kv) r[p] = u32x4{0u, 0u, 0u, 0u};
+      for (int p = 0; p < 8; ++p) {
+        const int off = kv ? voff + p * rstride + k0 * 2 : 0x7ffffff0;
+        r[p] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
       }
     } else {
       const int k = k0 + (tid & 7) * 8;
@@ -171,26 +170,29 @@ struct SliceLoader {
   }
 };
 
-// One 64-wide K stage of the wave's 128 x 128 tile from LDS.
-__device__ __forceinline__ void mma_stage(const u16 (*sa)[PITCH], const u16 (*sb)[PITCH],
-                                          floatx16 (&acc)[4][4], int wi, int wj, int lane) {
+// Fragments of one 16-wide K sub-step: 4 A tiles and 4 B tiles of 32 rows.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void load_frags(const u16 (*sa)[PITCH], const u16 (*sb)[PITCH], int kk,
+                                           int wi, int wj, int lane, Frags& f) {
   const int r = lane & 31;
   const int kh = (lane >> 5) * 8;
 #pragma unroll
-  for (int kk = 0; kk < BK; kk += 16) {
-    bf16x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(&sa[wi * 128 + i * 32 + r][kk + kh]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(&sa[wi * 128 + i * 32 + r][kk + kh]);
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8*>(&sb[wj * 128 + j * 32 + r][kk + kh]);
+}
+
+__device__ __forceinline__ void mma_16(const Frags& f, floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(&sb[wj * 128 + j * 32 + r][kk + kh]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 __device__ __forceinline__ void zero_acc(floatx16 (&acc)[4][4]) {
@@ -202,11 +204,33 @@ __device__ __forceinline__ void zero_acc(floatx16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
+// Scheduling hints: interleave `n` instructions of class `mask` one by one
+// with MFMAs, so that in-order issue never blocks the MFMA pipe behind a burst
+// of memory instructions.  (mask: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read,
+// 0x200 DS write.)
+#define CCE_INTERLEAVE(mask, n)                           \
+  _Pragma("unroll") for (int _q = 0; _q < (n); ++_q) {    \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
+    __builtin_amdgcn_sched_group_barrier((mask), 1, 0);   \
+  }
+
 // acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles at A and B
 // (leading dimensions lda, ldb; rows beyond a_rows / b_rows are zero).
 // SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive; its
 // MFMAs are skipped (the stage still streams through LDS).
-template <bool VEC, bool SKIP>
+//
+// Schedule of iteration kt (stage cur = kt % 2 is multiplied):
+//   sub-step 0..2: 16 MFMAs each, interleaved with the LDS reads of the next
+//                  sub-step's fragments; sub-step 2 also writes K-slice kt+1
+//                  (held in registers) into stage cur^1, which every wave
+//                  finished reading before the previous iteration's barrier
+//   barrier        (stage cur^1 now holds slice kt+1 for everyone)
+//   sub-step 3:    16 MFMAs interleaved with the reads of slice kt+1's first
+//                  fragments and the global loads of slice kt+2
+// so each iteration is a single basic block and no LDS latency is exposed.
+// Past the last slice the loads re-read the last slice and the stores write
+// a stage nobody reads again; both are harmless.
+template <bool VEC, bool SKIP, bool KTAIL>
 __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, int a_rows,
                                           const u16* __restrict__ B, int ldb, int b_rows, int K,
                                           const int* __restrict__ kflags, int kflag_stride,
@@ -216,32 +240,46 @@ __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, in
   const int w = tid >> 6;
   const int wi = w & 1, wj = w >> 1;
   zero_acc(acc);
-  SliceLoader<VEC> la, lb;
+  SliceLoader<VEC, KTAIL> la, lb;
   la.init(A, lda, a_rows, K, tid);
   lb.init(B, ldb, b_rows, K, tid);
   const int nk = (K + BK - 1) / BK;
+  const int klast = (nk - 1) * BK;
   la.load(0, tid);
   lb.load(0, tid);
   la.store(sm.a[0], tid);
   lb.store(sm.b[0], tid);
+  la.load(min(BK, klast), tid);
+  lb.load(min(BK, klast), tid);
   __syncthreads();
-  if (nk > 1) {
-    la.load(BK, tid);
-    lb.load(BK, tid);
-  }
+  Frags f0, f1;
+  load_frags(sm.a[0], sm.b[0], 0, wi, wj, lane, f0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (!SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0)
-      mma_stage(sm.a[cur], sm.b[cur], acc, wi, wj, lane);
-    if (kt + 1 < nk) {
-      la.store(sm.a[cur ^ 1], tid);
-      lb.store(sm.b[cur ^ 1], tid);
-    }
+    const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
+    // sub-step 0
+    load_frags(sm.a[cur], sm.b[cur], 16, wi, wj, lane, f1);
+    if (active) mma_16(f0, acc);
+    CCE_INTERLEAVE(0x100, 8)
+    // sub-step 1
+    load_frags(sm.a[cur], sm.b[cur], 32, wi, wj, lane, f0);
+    if (active) mma_16(f1, acc);
+    CCE_INTERLEAVE(0x100, 8)
+    // sub-step 2 (+ slice kt+1 into the other stage)
+    load_frags(sm.a[cur], sm.b[cur], 48, wi, wj, lane, f1);
+    la.store(sm.a[cur ^ 1], tid);
+    lb.store(sm.b[cur ^ 1], tid);
+    if (active) mma_16(f0, acc);
+    CCE_INTERLEAVE(0x100, 4)
+    CCE_INTERLEAVE(0x300, 12)
     __syncthreads();
-    if (kt + 2 < nk) {
-      la.load((kt + 2) * BK, tid);
-      lb.load((kt + 2) * BK, tid);
-    }
+    // sub-step 3 (+ first fragments of slice kt+1, global loads of slice kt+2)
+    load_frags(sm.a[cur ^ 1], sm.b[cur ^ 1], 0, wi, wj, lane, f0);
+    const int kn = min((kt + 2) * BK, klast);
+    la.load(kn, tid);
+    lb.load(kn, tid);
+    if (active) mma_16(f1, acc);
+    CCE_INTERLEAVE(0x120, 16)
   }
 }
 

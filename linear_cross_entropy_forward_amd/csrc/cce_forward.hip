@@ -65,7 +65,7 @@ __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool KTAIL>
 __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const u16* __restrict__ W,
                                                const int* __restrict__ y, int M, int V, int D,
                                                int nMt, int nVt, int S, int T, int nlaunch,
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
   for (int t = split * T; t < t_end; ++t) {
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    gemm_tile<VEC, false>(W + (size_t)v0 * D, D, min(TILE, V - v0), Hb, D, hrows, D, nullptr, 0, sm,
+    gemm_tile<VEC, false, KTAIL>(W + (size_t)v0 * D, D, min(TILE, V - v0), Hb, D, hrows, D, nullptr, 0, sm,
                           acc);
     const int vw = v0 + wi * 128;  // first vocab row of this wave's half of the tile
     if (v0 + TILE > V)
@@ -164,12 +164,13 @@ __global__ __launch_bounds__(256) void k_fwd_merge(const float* __restrict__ par
 hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
   const int n = a.nMt * a.S;
   const int nlaunch = (n + 7) / 8 * 8;
-  if (a.vec)
-    hipLaunchKernelGGL(k_fwd<true>, dim3(nlaunch), dim3(NT), 0, st, a.H, a.W, a.y, a.M, a.V, a.D,
-                       a.nMt, a.nVt, a.S, a.T, nlaunch, a.part_m, a.part_s, a.tgt, a.Mpad);
-  else
-    hipLaunchKernelGGL(k_fwd<false>, dim3(nlaunch), dim3(NT), 0, st, a.H, a.W, a.y, a.M, a.V, a.D,
-                       a.nMt, a.nVt, a.S, a.T, nlaunch, a.part_m, a.part_s, a.tgt, a.Mpad);
+#define CCE_FWD(VEC, KT)                                                                          \
+  hipLaunchKernelGGL((k_fwd<VEC, KT>), dim3(nlaunch), dim3(NT), 0, st, a.H, a.W, a.y, a.M, a.V,     \
+                     a.D, a.nMt, a.nVt, a.S, a.T, nlaunch, a.part_m, a.part_s, a.tgt, a.Mpad)
+  if (!a.vec) CCE_FWD(false, false);
+  else if (a.D % BK != 0) CCE_FWD(true, true);
+  else CCE_FWD(true, false);
+#undef CCE_FWD
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, a.part_m, a.part_s,
