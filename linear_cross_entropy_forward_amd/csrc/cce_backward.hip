@@ -73,7 +73,8 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
     const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
     const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
     int vlen, int nMt, int nvt, int nlaunch, float filter_eps, float block_eps,
-    u16* __restrict__ G, u16* __restrict__ GT, int* __restrict__ flags, int Mpad, int Vc) {
+    u16* __restrict__ G, u16* __restrict__ GT, int* __restrict__ flags, int ldGT, int ldG,
+    int Vc) {
   __shared__ Smem sm;
   __shared__ float red[4];
   int mt, vt;
@@ -133,12 +134,16 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
   }
   if (tid == 0) *flag = 1;
 
+  // G (token rows, vocab contiguous): each lane stores its 4 consecutive vocab
+  // entries per (token, 8-row group) directly.  G^T (vocab rows, token
+  // contiguous) is staged through LDS so that it leaves as 16-byte rows.
+  __syncthreads();  // every wave is done with the operand stages
+  u16 (*tt)[TILE + 8] = reinterpret_cast<u16 (*)[TILE + 8]>(&sm);
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
-    u16* gt_col = GT + j;
-    u16* g_row = G + (size_t)j * Vc;
+    const int tj = wj * 128 + jj * 32 + (lane & 31);
+    u16* g_row = G + (size_t)(mt * TILE + tj) * ldG;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
 #pragma unroll
@@ -152,46 +157,76 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
           if (FILTER && p < filter_eps && !is_t) p = 0.f;
           g[e] = cf[jj] * (is_t ? p - 1.f : p);
         }
-        const int vl = vl0 + ii * 32 + 8 * q + 4 * half;
+        const int vt_row = wi * 128 + ii * 32 + 8 * q + 4 * half;  // tile-local vocab row
         u32x2 pk = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-        *reinterpret_cast<u32x2*>(g_row + vl) = pk;
-        gt_col[(size_t)(vl + 0) * Mpad] = (u16)(pk[0] & 0xffffu);
-        gt_col[(size_t)(vl + 1) * Mpad] = (u16)(pk[0] >> 16);
-        gt_col[(size_t)(vl + 2) * Mpad] = (u16)(pk[1] & 0xffffu);
-        gt_col[(size_t)(vl + 3) * Mpad] = (u16)(pk[1] >> 16);
+        *reinterpret_cast<u32x2*>(g_row + vl0 - wi * 128 + vt_row) = pk;
+        tt[vt_row + 0][tj] = (u16)(pk[0] & 0xffffu);
+        tt[vt_row + 1][tj] = (u16)(pk[0] >> 16);
+        tt[vt_row + 2][tj] = (u16)(pk[1] & 0xffffu);
+        tt[vt_row + 3][tj] = (u16)(pk[1] >> 16);
       }
     }
   }
+  __syncthreads();
+  // 256 vocab rows x 32 chunks of 8 tokens: 32 chunks per thread
+  u16* gt_tile = GT + (size_t)(vt * TILE) * ldGT + mt * TILE;
+#pragma unroll 8
+  for (int p = 0; p < 32; ++p) {
+    const int c = tid + 256 * p;
+    const int row = c >> 5, col = (c & 31) * 8;
+    *reinterpret_cast<u32x4*>(gt_tile + (size_t)row * ldGT + col) =
+        *reinterpret_cast<const u32x4*>(&tt[row][col]);
+  }
 }
 
-// C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k] with fp32 output.
-// kflags: per 256-wide K block of A-tile ta, flags[ta*fa + kb*fk] (null = all).
-template <bool ACCUM, bool SKIP>
-__global__ __launch_bounds__(NT, 1) void k_gemm_f32out(
-    const u16* __restrict__ A, int lda, int a_rows, const u16* __restrict__ B, int ldb, int b_rows,
-    int K, float* __restrict__ C, int ldc, int c_rows, int c_cols, int nA, int nB, int nlaunch,
-    const int* __restrict__ kflags, int fa, int fk) {
+// One fp32-output contraction C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k]
+// over an nA x nB tile grid launched as nl workgroups.
+struct GemmProb {
+  const u16* A;
+  int lda, a_rows;
+  const u16* B;
+  int ldb, b_rows;
+  int K;
+  float* C;
+  int ldc, c_rows, c_cols;
+  int nA, nB, nl;
+  const int* kflags;  // per 256-wide K block of A tile ta: kflags[ta*fa + kb*fk]
+  int fa, fk;
+  int accum;  // 1: C += result, 0: C = result
+};
+
+// The dh and dW contractions of one vocab chunk in a single launch: workgroups
+// [0, p0.nl) take p0 (dh, the longer K), the rest take p1 (dW).  Dispatching
+// the long tiles first lets the short ones fill the tail, so the two problems
+// together keep every CU busy (dh alone has too few output tiles).
+template <bool SKIP>
+__global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
   __shared__ Smem sm;
+  int b = blockIdx.x;
+  const bool second = b >= p0.nl;
+  const GemmProb p = second ? p1 : p0;
+  if (second) b -= p0.nl;
   int ta, tb;
-  if (!map_tile(blockIdx.x, nlaunch, nA, nB, 8, ta, tb)) return;
+  if (!map_tile(b, p.nl, p.nA, p.nB, 8, ta, tb)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   floatx16 acc[4][4];
-  gemm_tile<true, SKIP, false>(A + (size_t)ta * TILE * lda, lda, min(TILE, a_rows - ta * TILE),
-                        B + (size_t)tb * TILE * ldb, ldb, min(TILE, b_rows - tb * TILE), K,
-                        SKIP ? kflags + (size_t)ta * fa : nullptr, fk, sm, acc);
+  gemm_tile<true, SKIP, false>(p.A + (size_t)ta * TILE * p.lda, p.lda, min(TILE, p.a_rows - ta * TILE),
+                               p.B + (size_t)tb * TILE * p.ldb, p.ldb, min(TILE, p.b_rows - tb * TILE),
+                               p.K, SKIP ? p.kflags + (size_t)ta * p.fa : nullptr, p.fk, sm, acc);
+  const bool accum = p.accum != 0;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = ta * TILE + wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (row >= c_rows) continue;
-      float* crow = C + (size_t)row * ldc;
+      if (row >= p.c_rows) continue;
+      float* crow = p.C + (size_t)row * p.ldc;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int col = tb * TILE + wj * 128 + jj * 32 + (lane & 31);
-        if (col < c_cols) {
-          if (ACCUM) crow[col] += acc[ii][jj][r];
+        if (col < p.c_cols) {
+          if (accum) crow[col] += acc[ii][jj][r];
           else crow[col] = acc[ii][jj][r];
         }
       }
@@ -205,7 +240,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   const int nDt = a.Dpad / kTile;
   // h^T [Dpad, Mpad], zero padded
   hipLaunchKernelGGL(k_transpose, dim3(a.Mpad / 64, a.Dpad / 64), dim3(256), 0, st, a.H, a.M, a.D,
-                     a.D, a.HT, a.Dpad, a.Mpad, a.Mpad, (int)a.vec);
+                     a.D, a.HT, a.Dpad, a.Mpad, a.ldM, (int)a.vec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool filt = a.filter_eps > 0.f;
   for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
@@ -214,7 +249,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     const u16* Wc = a.W + (size_t)v0 * a.D;
     // 1. WT = W[chunk]^T, [Dpad, nvt*256] used of [Dpad, Vc]
     hipLaunchKernelGGL(k_transpose, dim3(nvt * kTile / 64, a.Dpad / 64), dim3(256), 0, st, Wc, vlen,
-                       a.D, a.D, a.WT, a.Dpad, nvt * kTile, a.Vc, (int)a.vec);
+                       a.D, a.D, a.WT, a.Dpad, nvt * kTile, a.ldV, (int)a.vec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 2. recompute + gradient tile
     {
@@ -222,7 +257,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
 #define CCE_RECOMPUTE(VEC, FILT, KT)                                                               \
   hipLaunchKernelGGL((k_recompute<VEC, FILT, KT>), dim3(nl), dim3(NT), 0, st, a.H, Wc, a.y, a.lse, \
                      a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, nl, a.filter_eps, a.block_eps, a.G,   \
-                     a.GT, a.flags, a.Mpad, a.Vc)
+                     a.GT, a.flags, a.ldM, a.ldV, a.Vc)
       const bool kt = a.D % BK != 0;
       if (!a.vec) {
         if (filt) CCE_RECOMPUTE(false, true, false); else CCE_RECOMPUTE(false, false, false);
@@ -234,32 +269,20 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
 #undef CCE_RECOMPUTE
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const bool skip = a.block_eps > 0.f;
-    const int fstride = a.Vc / kTile;
-    // 3. dW[chunk] = G^T h : A = GT [nvt*256 rows, K = Mpad], B = HT [Dpad rows, K = Mpad]
+    // 3+4. dh (+)= G W[chunk] and dW[chunk] = G^T h in one launch
+    //   dh: A = G [Mpad rows, K = nvt*256], B = WT [Dpad rows], C = dh
+    //   dW: A = GT [nvt*256 rows, K = Mpad], B = HT [Dpad rows], C = dW[v0:]
     {
-      const int n = nvt * nDt, nl = pad8(n);
-#define CCE_DW(SKIP)                                                                               \
-  hipLaunchKernelGGL((k_gemm_f32out<false, SKIP>), dim3(nl), dim3(NT), 0, st, a.GT, a.Mpad,         \
-                     nvt * kTile, a.HT, a.Mpad, a.Dpad, a.Mpad, a.dW + (size_t)v0 * a.D, a.D, vlen, \
-                     a.D, nvt, nDt, nl, a.flags, 1, fstride)
-      if (skip) CCE_DW(true); else CCE_DW(false);
-#undef CCE_DW
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    // 4. dh (+)= G W[chunk] : A = G [Mpad rows, K = nvt*256], B = WT [Dpad rows, K = nvt*256]
-    {
-      const int n = a.nMt * nDt, nl = pad8(n);
-#define CCE_DH(ACC, SKIP)                                                                          \
-  hipLaunchKernelGGL((k_gemm_f32out<ACC, SKIP>), dim3(nl), dim3(NT), 0, st, a.G, a.Vc, a.Mpad,      \
-                     a.WT, a.Vc, a.Dpad, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, nl, a.flags, \
-                     fstride, 1)
-      if (v0 == 0) {
-        if (skip) CCE_DH(false, true); else CCE_DH(false, false);
-      } else {
-        if (skip) CCE_DH(true, true); else CCE_DH(true, false);
-      }
-#undef CCE_DH
+      const bool skip = a.block_eps > 0.f;
+      const int fstride = a.Vc / kTile;
+      GemmProb dh{a.G, a.ldV, a.Mpad, a.WT, a.ldV, a.Dpad, nvt * kTile, a.dh, a.D, a.M, a.D,
+                  a.nMt, nDt, pad8(a.nMt * nDt), a.flags, fstride, 1, v0 == 0 ? 0 : 1};
+      GemmProb dw{a.GT, a.ldM, nvt * kTile, a.HT, a.ldM, a.Dpad, a.Mpad, a.dW + (size_t)v0 * a.D,
+                  a.D, vlen, a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0};
+      if (skip)
+        hipLaunchKernelGGL(k_grads<true>, dim3(dh.nl + dw.nl), dim3(NT), 0, st, dh, dw);
+      else
+        hipLaunchKernelGGL(k_grads<false>, dim3(dh.nl + dw.nl), dim3(NT), 0, st, dh, dw);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }

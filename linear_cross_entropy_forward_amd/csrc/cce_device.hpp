@@ -6,10 +6,10 @@
 //   workgroup tile   256 (A rows) x 256 (B rows), 256 threads = 4 waves
 //   wave tile        128 x 128 = 4 x 4 MFMA tiles of 32x32, fp32 accumulators
 //   MFMA             v_mfma_f32_32x32x16_bf16 (8 bf16 of K per lane)
-//   K pipeline       64 bf16 per stage, two LDS stages, global loads for
-//                    stage k+2 in flight while stage k is multiplied
-//   LDS              rows padded to 144 B so that the 16-byte fragment reads of
-//                    32 consecutive rows hit distinct banks
+//   K pipeline       32 bf16 per stage, a ring of 4 LDS stages filled by
+//                    direct-to-LDS buffer loads issued 3 stages ahead
+//   LDS              64-byte rows, 16-byte chunks XOR-swizzled by row so that
+//                    the fragment reads of 8 consecutive rows hit distinct banks
 //
 // Accumulator layout of one 32x32 MFMA tile (lane l, register r):
 //   i = 8*(r/4) + 4*(l/32) + (r%4),   j = l%32
@@ -32,15 +32,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int TILE = 256;
-constexpr int BK = 64;
-constexpr int PITCH = BK + 8;
+constexpr int BK = 32;                           // K elements per LDS stage
+constexpr int NSTAGE = 4;                        // LDS ring depth
+constexpr int HALF_BYTES = TILE * BK * 2;        // one operand of one stage: 16 KB
+constexpr int STAGE_BYTES = 2 * HALF_BYTES;      // A then B: 32 KB
 constexpr int NT = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
+// The operand ring (4 x 32 KB) and, after the K loop, epilogue staging of up
+// to 256 x 264 bf16.
 struct __align__(16) Smem {
-  u16 a[2][TILE][PITCH];
-  u16 b[2][TILE][PITCH];
+  unsigned char raw[NSTAGE * STAGE_BYTES > TILE * (TILE + 8) * 2 ? NSTAGE * STAGE_BYTES
+                                                                 : TILE * (TILE + 8) * 2];
 };
 
 // ---------------------------------------------------------------------------
@@ -89,17 +93,8 @@ __device__ __forceinline__ bool map_tile(int bid, int nlaunch, int nA, int nB, i
   return true;
 }
 
-// ---------------------------------------------------------------------------
-// global -> register -> LDS staging of one 256 x 64 K-slice of an operand
-// ---------------------------------------------------------------------------
-// Thread t moves rows (t/8) + 32p, p = 0..7, bytes 16*(t%8) .. +15 of the
-// slice.  Rows >= rows_valid and columns >= K read as zero.
-//
-// VEC (K % 8 == 0, 16-byte aligned rows): raw buffer loads over a resource
-// that ends at row rows_valid, so rows past it read as zero in hardware with
-// no branch (every byte offset is in the range-checked VGPR offset).  Only a K tail
-// (K % 64 != 0) needs a per-chunk select.  Otherwise elements are loaded one
-// by one with explicit bounds checks (a slow path for odd D).
+// Buffer resource over [base, base + bytes): loads whose (range-checked) VGPR
+// offset falls past the end return zero.  The scalar offset is always 0.
 // base and bytes are workgroup-uniform (kernel arguments and blockIdx only);
 // readfirstlane states that, so the descriptor lives in SGPRs and the loads
 // need no per-lane waterfall loop.
@@ -112,79 +107,99 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
                                            0x00020000);
 }
 
-template <bool VEC, bool KTAIL>
-struct SliceLoader {
-  const u16* base;
-  int ld;
-  int rows_valid;
-  int K;
+// ---------------------------------------------------------------------------
+// LDS layout of one operand of one stage: 256 rows x 64 bytes (32 bf16 of K).
+// Row r's 16-byte chunk c (K elements 8c .. 8c+7) sits at position
+// c ^ swz(r) of the row, swz(r) = (r >> 1) & 3.  Eight consecutive rows then
+// cover all 32 banks for a given chunk.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
+
+// Direct-to-LDS loads of one 256 x 32 K-slice of a row-major operand.  Wave w
+// moves rows 64w .. 64w+63 with 4 instructions of 16 rows; in each, lane L
+// fills LDS bytes 16L .. 16L+15 (row 16p + L/4 of the instruction, position
+// L%4), so it fetches global chunk (L%4) ^ swz(row).  The buffer resource ends
+// at row rows_valid: rows past it read as zero, and so does a chunk at k >= K
+// (K tail, K % 8 == 0), which is pointed past the resource.
+template <bool KTAIL>
+struct DmaOperand {
   __amdgpu_buffer_rsrc_t rsrc;
-  int voff;     // byte offset of this thread's first chunk at k = 0
-  int rstride;  // bytes between this thread's rows (32 rows)
-  u32x4 r[8];
+  int voff;     // byte offset of this lane's chunk for instruction 0 at k = 0
+  int pstride;  // bytes between instructions (16 rows)
+  int c8;       // this lane's chunk index * 8 (K elements)
+  int K;
 
-  __device__ __forceinline__ void init(const u16* b, int ld_, int rows, int K_, int tid) {
-    base = b;
-    ld = ld_;
-    rows_valid = rows;
+  __device__ __forceinline__ void init(const u16* base, int ld, int rows, int K_, int lane, int w) {
+    rsrc = make_rsrc(base, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld * 2u);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);  // = (L%4) ^ swz(row) for every instruction
+    const int row0 = 64 * w + (lane >> 2);
+    voff = row0 * ld * 2 + c * 16;
+    pstride = 16 * ld * 2;
+    c8 = c * 8;
     K = K_;
-    if (VEC) {
-      rsrc = make_rsrc(b, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld_ * 2u);
-      voff = ((tid >> 3) * ld_ + (tid & 7) * 8) * 2;
-      rstride = 32 * ld_ * 2;
-    }
   }
 
-  // Issues the loads of K-slice k0 (one global load per row this thread moves).
-  __device__ __forceinline__ void load(int k0, int tid) {
-    if (VEC) {
-      // the whole offset rides in the VGPR offset (always range-checked);
-      // the scalar offset stays 0.  A chunk at k >= K (K tail, K % 8 == 0) is
-      // pointed past the resource so that it reads as zero.
-      const bool kv = !KTAIL || k0 + (tid & 7) * 8 < K;
+  // Issue the 4 loads of K-slice k0 into the operand region `dst` of a stage.
+  __device__ __forceinline__ void issue(int k0, unsigned char* dst, int w) const {
+    const bool kv = !KTAIL || k0 + c8 < K;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int off = kv ? voff + p * rstride + k0 * 2 : 0x7ffffff0;
-        r[p] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-      }
-    } else {
-      const int k = k0 + (tid & 7) * 8;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int row = (tid >> 3) + 32 * p;
-        unsigned e[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          e[q] = (row < rows_valid && k + q < K) ? base[(size_t)row * ld + k + q] : 0u;
-        r[p] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                     e[6] | (e[7] << 16)};
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int off = kv ? voff + p * pstride + k0 * 2 : 0x7ffffff0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, to_lds(dst + (64 * w + 16 * p) * 64), 16, off,
+                                               0, 0, 0);
     }
-  }
-
-  __device__ __forceinline__ void store(u16 (*s)[PITCH], int tid) const {
-    const int c = (tid & 7) * 8;
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-      *reinterpret_cast<u32x4*>(&s[(tid >> 3) + 32 * p][c]) = r[p];
   }
 };
+
+// Element-by-element loads of one K-slice into the same swizzled layout (the
+// path for odd D or 16-byte-misaligned operands; not pipelined).
+__device__ __forceinline__ void slow_slice(const u16* __restrict__ base, int ld, int rows_valid,
+                                           int K, int k0, unsigned char* dst, int tid) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int idx = tid + 256 * p;  // 1024 chunks: row idx/4, chunk idx%4
+    const int row = idx >> 2, c = idx & 3;
+    const int k = k0 + c * 8;
+    unsigned e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      e[q] = (row < rows_valid && k + q < K) ? base[(size_t)row * ld + k + q] : 0u;
+    *reinterpret_cast<u32x4*>(dst + row * 64 + ((c ^ swz(row)) << 4)) =
+        u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+  }
+}
 
 // Fragments of one 16-wide K sub-step: 4 A tiles and 4 B tiles of 32 rows.
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void load_frags(const u16 (*sa)[PITCH], const u16 (*sb)[PITCH], int kk,
-                                           int wi, int wj, int lane, Frags& f) {
-  const int r = lane & 31;
-  const int kh = (lane >> 5) * 8;
+// Per-lane byte offsets of the fragment rows inside a stage.
+struct FragAddr {
+  int a, b;    // row part of the A / B addresses (tile 0)
+  int k0, k1;  // chunk part for sub-step 0 (K 0..15) and sub-step 1 (K 16..31)
+  __device__ __forceinline__ void init(int lane, int wi, int wj) {
+    const int r = lane & 31, half = lane >> 5;
+    const int sw = (r >> 1) & 3;  // swz of every row this lane reads
+    a = (wi * 128 + r) * 64;
+    b = HALF_BYTES + (wj * 128 + r) * 64;
+    k0 = (half ^ sw) << 4;
+    k1 = ((2 + half) ^ sw) << 4;
+  }
+};
+
+__device__ __forceinline__ void load_frags(const unsigned char* stage, const FragAddr& fa, int kpart,
+                                           Frags& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const bf16x8*>(&sa[wi * 128 + i * 32 + r][kk + kh]);
+    f.a[i] = *reinterpret_cast<const bf16x8*>(stage + fa.a + i * 32 * 64 + kpart);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    f.b[j] = *reinterpret_cast<const bf16x8*>(&sb[wj * 128 + j * 32 + r][kk + kh]);
+    f.b[j] = *reinterpret_cast<const bf16x8*>(stage + fa.b + j * 32 * 64 + kpart);
 }
 
 __device__ __forceinline__ void mma_16(const Frags& f, floatx16 (&acc)[4][4]) {
@@ -204,10 +219,26 @@ __device__ __forceinline__ void zero_acc(floatx16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+#define CCE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier for the operand ring: waits for this wave's LDS reads
+// (lgkmcnt 0) but not for its in-flight direct-to-LDS loads; the caller has
+// already waited (CCE_WAIT_VMCNT) for the loads whose data the next reads
+// need.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt / expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Scheduling hints: interleave `n` instructions of class `mask` one by one
 // with MFMAs, so that in-order issue never blocks the MFMA pipe behind a burst
-// of memory instructions.  (mask: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read,
-// 0x200 DS write.)
+// of memory instructions.  (mask: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read.)
 #define CCE_INTERLEAVE(mask, n)                           \
   _Pragma("unroll") for (int _q = 0; _q < (n); ++_q) {    \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
@@ -217,19 +248,18 @@ __device__ __forceinline__ void zero_acc(floatx16 (&acc)[4][4]) {
 // acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles at A and B
 // (leading dimensions lda, ldb; rows beyond a_rows / b_rows are zero).
 // SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive; its
-// MFMAs are skipped (the stage still streams through LDS).
+// MFMAs are skipped (its slices still stream through LDS).
 //
-// Schedule of iteration kt (stage cur = kt % 2 is multiplied):
-//   sub-step 0..2: 16 MFMAs each, interleaved with the LDS reads of the next
-//                  sub-step's fragments; sub-step 2 also writes K-slice kt+1
-//                  (held in registers) into stage cur^1, which every wave
-//                  finished reading before the previous iteration's barrier
-//   barrier        (stage cur^1 now holds slice kt+1 for everyone)
-//   sub-step 3:    16 MFMAs interleaved with the reads of slice kt+1's first
-//                  fragments and the global loads of slice kt+2
-// so each iteration is a single basic block and no LDS latency is exposed.
-// Past the last slice the loads re-read the last slice and the stores write
-// a stage nobody reads again; both are harmless.
+// VEC path, iteration kt (slice kt sits in stage kt % 4):
+//   issue the direct-to-LDS loads of slice kt+3 into stage (kt+3) % 4 (last
+//     read in iteration kt-1, before the barrier that ended it)
+//   sub-step 0: 16 MFMAs on fragments read earlier, interleaved with those
+//     loads and the LDS reads of sub-step 1's fragments
+//   wait until this wave's loads of slice kt+1 have landed, then barrier
+//   sub-step 1: 16 MFMAs interleaved with the reads of slice kt+1's first
+//     fragments
+// Slices past the last one are clamped to it (their stages are no longer
+// read); the loop ends by draining every load and a barrier, so LDS is free.
 template <bool VEC, bool SKIP, bool KTAIL>
 __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, int a_rows,
                                           const u16* __restrict__ B, int ldb, int b_rows, int K,
@@ -240,46 +270,61 @@ __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, in
   const int w = tid >> 6;
   const int wi = w & 1, wj = w >> 1;
   zero_acc(acc);
-  SliceLoader<VEC, KTAIL> la, lb;
-  la.init(A, lda, a_rows, K, tid);
-  lb.init(B, ldb, b_rows, K, tid);
+  FragAddr fa;
+  fa.init(lane, wi, wj);
+  unsigned char* ring = sm.raw;
   const int nk = (K + BK - 1) / BK;
-  const int klast = (nk - 1) * BK;
-  la.load(0, tid);
-  lb.load(0, tid);
-  la.store(sm.a[0], tid);
-  lb.store(sm.b[0], tid);
-  la.load(min(BK, klast), tid);
-  lb.load(min(BK, klast), tid);
-  __syncthreads();
-  Frags f0, f1;
-  load_frags(sm.a[0], sm.b[0], 0, wi, wj, lane, f0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
-    // sub-step 0
-    load_frags(sm.a[cur], sm.b[cur], 16, wi, wj, lane, f1);
-    if (active) mma_16(f0, acc);
-    CCE_INTERLEAVE(0x100, 8)
-    // sub-step 1
-    load_frags(sm.a[cur], sm.b[cur], 32, wi, wj, lane, f0);
-    if (active) mma_16(f1, acc);
-    CCE_INTERLEAVE(0x100, 8)
-    // sub-step 2 (+ slice kt+1 into the other stage)
-    load_frags(sm.a[cur], sm.b[cur], 48, wi, wj, lane, f1);
-    la.store(sm.a[cur ^ 1], tid);
-    lb.store(sm.b[cur ^ 1], tid);
-    if (active) mma_16(f0, acc);
-    CCE_INTERLEAVE(0x100, 4)
-    CCE_INTERLEAVE(0x300, 12)
+  if (VEC) {
+    DmaOperand<KTAIL> da, db;
+    da.init(A, lda, a_rows, K, lane, w);
+    db.init(B, ldb, b_rows, K, lane, w);
+    const int klast = (nk - 1) * BK;
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s) {
+      const int k = min(s * BK, klast);
+      da.issue(k, ring + s * STAGE_BYTES, w);
+      db.issue(k, ring + s * STAGE_BYTES + HALF_BYTES, w);
+    }
+    CCE_WAIT_VMCNT(16);  // slice 0 landed (slices 1 and 2 may be in flight)
+    ring_barrier();
+    Frags f0, f1;
+    load_frags(ring, fa, fa.k0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      unsigned char* cur = ring + (kt & (NSTAGE - 1)) * STAGE_BYTES;
+      unsigned char* nxt = ring + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES;
+      unsigned char* far = ring + ((kt + 3) & (NSTAGE - 1)) * STAGE_BYTES;
+      const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
+      // sub-step 0
+      const int kn = min((kt + 3) * BK, klast);
+      da.issue(kn, far, w);
+      db.issue(kn, far + HALF_BYTES, w);
+      load_frags(cur, fa, fa.k1, f1);
+      if (active) mma_16(f0, acc);
+      CCE_INTERLEAVE(0x020, 8)
+      CCE_INTERLEAVE(0x100, 8)
+      CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slices kt+2, kt+3 may be in flight)
+      ring_barrier();
+      // sub-step 1
+      load_frags(nxt, fa, fa.k0, f0);
+      if (active) mma_16(f1, acc);
+      CCE_INTERLEAVE(0x100, 8)
+    }
+    CCE_WAIT_VMCNT(0);
     __syncthreads();
-    // sub-step 3 (+ first fragments of slice kt+1, global loads of slice kt+2)
-    load_frags(sm.a[cur ^ 1], sm.b[cur ^ 1], 0, wi, wj, lane, f0);
-    const int kn = min((kt + 2) * BK, klast);
-    la.load(kn, tid);
-    lb.load(kn, tid);
-    if (active) mma_16(f1, acc);
-    CCE_INTERLEAVE(0x120, 16)
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
+      __syncthreads();
+      slow_slice(A, lda, a_rows, K, kt * BK, ring, tid);
+      slow_slice(B, ldb, b_rows, K, kt * BK, ring + HALF_BYTES, tid);
+      __syncthreads();
+      Frags f;
+      load_frags(ring, fa, fa.k0, f);
+      if (active) mma_16(f, acc);
+      load_frags(ring, fa, fa.k1, f);
+      if (active) mma_16(f, acc);
+    }
+    __syncthreads();
   }
 }
 

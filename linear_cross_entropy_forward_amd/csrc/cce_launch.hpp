@@ -15,6 +15,10 @@ constexpr int kTile = 256;
 constexpr int kVocabChunk = 16384;
 // Doubles per pair in the epilogue's pair table.
 constexpr int kPairStride = 16;
+// Extra bf16 elements per row of every backward workspace matrix: keeps row
+// pitches off powers of two, so the rows one load or store instruction
+// touches spread over the memory channels.
+constexpr int kPitchPad = 64;
 
 struct FwdArgs {
   const u16* H;
@@ -55,14 +59,15 @@ struct BwdArgs {
   const float* coef;
   int M, V, D;
   int nMt, Mpad, Dpad, Vc;
+  int ldM, ldV;  // row pitches (elements) of the M-long and Vc-long workspace rows
   bool vec;
   float filter_eps, block_eps;
   float* dh;
   float* dW;
-  u16* HT;     // [Dpad, Mpad]
-  u16* WT;     // [Dpad, Vc]
-  u16* G;      // [Mpad, Vc]
-  u16* GT;     // [Vc, Mpad]
+  u16* HT;     // [Dpad, Mpad], pitch ldM
+  u16* WT;     // [Dpad, Vc], pitch ldV
+  u16* G;      // [Mpad, Vc], pitch ldV
+  u16* GT;     // [Vc, Mpad], pitch ldM
   int* flags;  // [nMt, Vc / kTile]
   unsigned* status;
 };
