@@ -34,7 +34,46 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --calibrate-copy run into --traffic-json; no GPU use")
     return ap.parse_args()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, workload: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the forward kernel, scaled by
+    what the same counters read for the 1 GiB copy kernel of the same run."""
+    import csv
+    from linear_cross_entropy_forward_amd import binding as B
+
+    def per_dispatch(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        return acc
+
+    res = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        d = per_dispatch(path, counter)
+        fwd = [v for (i, n), v in d.items() if "k_fwd<" in n]
+        copy = [v for (i, n), v in d.items() if "copyBuffer" in n or "copy" in n.lower()]
+        copy = [v for v in copy if v > 1e5]          # the 1 GiB copy, not small transfers
+        if not fwd or not copy:
+            raise SystemExit(f"{path}: no forward or copy dispatch with {counter}")
+        scale = (1 << 30) / (max(copy) * 1024.0)      # true bytes per counted byte
+        res[counter] = {"kib_per_launch": sum(fwd) / len(fwd), "copy_kib": max(copy),
+                        "scale": scale, "bytes_per_launch": sum(fwd) / len(fwd) * 1024.0 * scale}
+    out = {"workload": workload, "kernel": "k_fwd", "kernel_source_hash": B.kernel_source_hash(),
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl, rows: int):
@@ -73,6 +112,9 @@ def cpu_baseline(wl, rows: int):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic_json, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the head is built and "
               f"measured on a single MI355X, with no multi-GPU path.", file=sys.stderr)
@@ -187,6 +229,13 @@ def main():
     }
     del dh, dW
     torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
