@@ -9,7 +9,7 @@
 
 #include <mutex>
 
-#include "../../include/flashcce.h"
+#include "flashcce.h"
 #include "cce_launch.hpp"
 
 namespace {
@@ -38,8 +38,10 @@ void fwd_split(int64_t nMt, int64_t nVt, int& S, int& T) {
   T = (int)t;
   S = (int)((nVt + t - 1) / t);
 }
-// Upper bound of S over all V for this M (so the workspace does not grow with V).
-int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 1; }
+// Upper bound of the partial slots over all V for this M (so the workspace does
+// not grow with V): the splits over the full vocab tiles plus one slot for a
+// ragged last tile.
+int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
@@ -73,23 +75,30 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   return L;
 }
 
-// gfx950 check of the current device, cached per device id.
-cce_status device_ok() {
+// gfx950 check of the current device and its compute-unit count, cached per
+// device id.
+cce_status device_ok(int* ncu = nullptr) {
   static std::mutex mu;
   static int cache[64];  // 0 unknown, 1 ok, 2 not ok
+  static int cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CCE_EDEVICE;
   if (dev < 64) {
     std::lock_guard<std::mutex> g(mu);
-    if (cache[dev] == 1) return CCE_OK;
+    if (cache[dev] == 1) {
+      if (ncu) *ncu = cus[dev];
+      return CCE_OK;
+    }
     if (cache[dev] == 2) return CCE_EDEVICE;
   }
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CCE_EDEVICE;
   const bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+  if (ncu) *ncu = p.multiProcessorCount;
   if (dev < 64) {
     std::lock_guard<std::mutex> g(mu);
     cache[dev] = ok ? 1 : 2;
+    cus[dev] = p.multiProcessorCount;
   }
   return ok ? CCE_OK : CCE_EDEVICE;
 }
@@ -138,7 +147,8 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
   a.D = (int)D;
   a.nMt = (int)L.nMt;
   a.nVt = (int)((V + kTile - 1) / kTile);
-  fwd_split(a.nMt, a.nVt, a.S, a.T);
+  a.S = a.T = 0;
+  if (V / kTile > 0) fwd_split(a.nMt, V / kTile, a.S, a.T);  // over the full vocab tiles
   a.Mpad = (int)L.Mpad;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
   a.part_m = reinterpret_cast<float*>(base + L.part_m);
@@ -193,10 +203,12 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
   const Layout L = layout(M, V, D);
   if (ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return CCE_EWORKSPACE;
-  const cce_status ds = device_ok();
+  int ncu = 0;
+  const cce_status ds = device_ok(&ncu);
   if (ds != CCE_OK) return ds;
   char* base = static_cast<char*>(ws);
   cce::BwdArgs a{};
+  a.ncu8 = ncu >= 8 ? ncu / 8 * 8 : 8;
   a.H = static_cast<const cce::u16*>(h);
   a.W = static_cast<const cce::u16*>(W);
   a.y = y;

@@ -65,22 +65,32 @@ __global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ src, 
   }
 }
 
-// Recompute one 256 (vocab) x 256 (token) logit tile of the chunk and write its
-// gradient tile.  A = W rows of the chunk, B = h rows, so each lane owns one
+// Recompute 256 (vocab) x 256 (token) logit tiles of the chunk and write their
+// gradient tiles.  A = W rows of the chunk, B = h rows, so each lane owns one
 // token (lse, coef, target in registers) and 16 vocab entries per MFMA tile.
+// Persistent: P workgroups (a multiple of 8, at most one per CU) walk the
+// tiles in steps of P, so the stores of one tile drain while the next tile's
+// K loop runs.  At step t workgroup b takes logical tile
+// P*t + (b % 8)*(P/8) + b/8 of the grouped raster, i.e. each XCD works on a
+// contiguous run of tiles.
 template <bool VEC, bool FILTER, bool KTAIL>
 __global__ __launch_bounds__(NT, 1) void k_recompute(
     const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
     const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
-    int vlen, int nMt, int nvt, int nlaunch, float filter_eps, float block_eps,
+    int vlen, int nMt, int nvt, int P, float filter_eps, float block_eps,
     u16* __restrict__ G, u16* __restrict__ GT, int* __restrict__ flags, int ldGT, int ldG,
     int Vc) {
   __shared__ Smem sm;
   __shared__ float red[4];
-  int mt, vt;
-  if (!map_tile(blockIdx.x, nlaunch, nMt, nvt, 8, mt, vt)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+  const int ntiles = nMt * nvt;
+  const int b = blockIdx.x;
+  for (int base = 0; base < ntiles; base += P) {
+  const int L = base + (b & 7) * (P >> 3) + (b >> 3);
+  if (L >= ntiles) break;
+  int mt, vt;
+  raster_tile(L, nMt, nvt, 8, mt, vt);
 
   floatx16 acc[4][4];
   gemm_tile<VEC, false, KTAIL>(Wc + (size_t)vt * TILE * D, D, min(TILE, vlen - vt * TILE),
@@ -129,53 +139,75 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
     const bool keep = (red[0] + red[1] + red[2] + red[3]) > 0.f;
     if (!keep) {
       if (tid == 0) *flag = 0;
-      return;
+      continue;
     }
   }
   if (tid == 0) *flag = 1;
 
-  // G (token rows, vocab contiguous): each lane stores its 4 consecutive vocab
-  // entries per (token, 8-row group) directly.  G^T (vocab rows, token
-  // contiguous) is staged through LDS so that it leaves as 16-byte rows.
-  __syncthreads();  // every wave is done with the operand stages
-  u16 (*tt)[TILE + 8] = reinterpret_cast<u16 (*)[TILE + 8]>(&sm);
+  // The gradient tile leaves in two passes through LDS so that every global
+  // store is a 16-byte piece of a row: first G (token rows, vocab contiguous),
+  // then G^T (vocab rows, token contiguous).  g is formed from the softmax
+  // values kept in acc in each pass.
+  u16 (*st)[TILE + 8] = reinterpret_cast<u16 (*)[TILE + 8]>(&sm);
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
+  auto grad4 = [&](int ii, int jj, int q) -> u32x2 {
+    float g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float p = acc[ii][jj][4 * q + e];
+      const bool is_t = wave_has_tgt && (off[jj] == ii * 32 + 8 * q + e);
+      if (FILTER && p < filter_eps && !is_t) p = 0.f;
+      g[e] = cf[jj] * (is_t ? p - 1.f : p);
+    }
+    return u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+  };
+  __syncthreads();  // every wave is done with the operand stages
+  // pass 1: st[token][vocab]
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int tj = wj * 128 + jj * 32 + (lane & 31);
-    u16* g_row = G + (size_t)(mt * TILE + tj) * ldG;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q + e;
-          float p = acc[ii][jj][r];
-          const bool is_t = wave_has_tgt && (off[jj] == ii * 32 + 8 * q + e);
-          if (FILTER && p < filter_eps && !is_t) p = 0.f;
-          g[e] = cf[jj] * (is_t ? p - 1.f : p);
-        }
-        const int vt_row = wi * 128 + ii * 32 + 8 * q + 4 * half;  // tile-local vocab row
-        u32x2 pk = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-        *reinterpret_cast<u32x2*>(g_row + vl0 - wi * 128 + vt_row) = pk;
-        tt[vt_row + 0][tj] = (u16)(pk[0] & 0xffffu);
-        tt[vt_row + 1][tj] = (u16)(pk[0] >> 16);
-        tt[vt_row + 2][tj] = (u16)(pk[1] & 0xffffu);
-        tt[vt_row + 3][tj] = (u16)(pk[1] >> 16);
-      }
-    }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(&st[tj][wi * 128 + ii * 32 + 8 * q + 4 * half]) = grad4(ii, jj, q);
   }
   __syncthreads();
-  // 256 vocab rows x 32 chunks of 8 tokens: 32 chunks per thread
+  u16* g_tile = G + (size_t)(mt * TILE) * ldG + vt * TILE;
+#pragma unroll 8
+  for (int p = 0; p < 32; ++p) {  // 256 token rows x 32 chunks of 8 vocab entries
+    const int c = tid + 256 * p;
+    const int row = c >> 5, col = (c & 31) * 8;
+    *reinterpret_cast<u32x4*>(g_tile + (size_t)row * ldG + col) =
+        *reinterpret_cast<const u32x4*>(&st[row][col]);
+  }
+  __syncthreads();
+  // pass 2: st[vocab][token]
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int tj = wj * 128 + jj * 32 + (lane & 31);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int vr = wi * 128 + ii * 32 + 8 * q + 4 * half;  // tile-local vocab row
+        const u32x2 pk = grad4(ii, jj, q);
+        st[vr + 0][tj] = (u16)(pk[0] & 0xffffu);
+        st[vr + 1][tj] = (u16)(pk[0] >> 16);
+        st[vr + 2][tj] = (u16)(pk[1] & 0xffffu);
+        st[vr + 3][tj] = (u16)(pk[1] >> 16);
+      }
+  }
+  __syncthreads();
   u16* gt_tile = GT + (size_t)(vt * TILE) * ldGT + mt * TILE;
 #pragma unroll 8
-  for (int p = 0; p < 32; ++p) {
+  for (int p = 0; p < 32; ++p) {  // 256 vocab rows x 32 chunks of 8 tokens
     const int c = tid + 256 * p;
     const int row = c >> 5, col = (c & 31) * 8;
     *reinterpret_cast<u32x4*>(gt_tile + (size_t)row * ldGT + col) =
-        *reinterpret_cast<const u32x4*>(&tt[row][col]);
+        *reinterpret_cast<const u32x4*>(&st[row][col]);
+  }
+  __syncthreads();  // staging reads done before the next tile's loads overwrite LDS
   }
 }
 
@@ -253,10 +285,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // 2. recompute + gradient tile
     {
-      const int n = a.nMt * nvt, nl = pad8(n);
+      const int n = a.nMt * nvt;
+      const int P = pad8(n) < a.ncu8 ? pad8(n) : a.ncu8;  // persistent workgroups
 #define CCE_RECOMPUTE(VEC, FILT, KT)                                                               \
-  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT>), dim3(nl), dim3(NT), 0, st, a.H, Wc, a.y, a.lse, \
-                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, nl, a.filter_eps, a.block_eps, a.G,   \
+  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT>), dim3(P), dim3(NT), 0, st, a.H, Wc, a.y, a.lse,  \
+                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, P, a.filter_eps, a.block_eps, a.G,    \
                      a.GT, a.flags, a.ldM, a.ldV, a.Vc)
       const bool kt = a.D % BK != 0;
       if (!a.vec) {

@@ -77,6 +77,17 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 // logical order is a grouped raster (GA 'a' tiles, then the next 'b') so the
 // workgroups sharing one XCD's L2 share both A and B tiles.  The launch grid
 // is padded to a multiple of 8; extra workgroups return false.
+// Logical tile index L -> (ta, tb) in the grouped raster described above.
+__device__ __forceinline__ void raster_tile(int L, int nA, int nB, int GA, int& ta, int& tb) {
+  const int ga = GA < nA ? GA : nA;
+  const int group = L / (ga * nB);
+  const int first = group * ga;
+  const int gsize = (nA - first) < ga ? (nA - first) : ga;
+  const int idx = L - group * ga * nB;
+  ta = first + idx % gsize;
+  tb = idx / gsize;
+}
+
 __device__ __forceinline__ bool map_tile(int bid, int nlaunch, int nA, int nB, int GA,
                                          int& ta, int& tb) {
   const int n = nA * nB;
@@ -110,10 +121,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // ---------------------------------------------------------------------------
 // LDS layout of one operand of one stage: 256 rows x 64 bytes (32 bf16 of K).
 // Row r's 16-byte chunk c (K elements 8c .. 8c+7) sits at position
-// c ^ swz(r) of the row, swz(r) = (r >> 1) & 3.  Eight consecutive rows then
-// cover all 32 banks for a given chunk.
+// c ^ swz(r) of the row, with
+//   swz(r) = ((r1 ^ r2) | (r2 ^ r3) << 1)   (r1, r2, r3: bits 1..3 of r).
+// For one chunk index, 8 consecutive rows (from a multiple of 8) land in 8
+// distinct 16-byte bank groups of 32 banks, and 16 consecutive rows (from a
+// multiple of 16) in 16 distinct groups of 64 banks, so the fragment reads are
+// conflict-free whether the LDS serves 8 or 16 lanes of a 16-byte read per
+// clock.  swz depends only on row bits 1..3.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -135,7 +153,8 @@ struct DmaOperand {
 
   __device__ __forceinline__ void init(const u16* base, int ld, int rows, int K_, int lane, int w) {
     rsrc = make_rsrc(base, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld * 2u);
-    const int c = (lane & 3) ^ ((lane >> 3) & 3);  // = (L%4) ^ swz(row) for every instruction
+    // row bits 0..3 are lane bits 2..5, so swz(row) = swz(lane >> 2) for every instruction
+    const int c = (lane & 3) ^ swz(lane >> 2);
     const int row0 = 64 * w + (lane >> 2);
     voff = row0 * ld * 2 + c * 16;
     pstride = 16 * ld * 2;
@@ -184,7 +203,7 @@ struct FragAddr {
   int k0, k1;  // chunk part for sub-step 0 (K 0..15) and sub-step 1 (K 16..31)
   __device__ __forceinline__ void init(int lane, int wi, int wj) {
     const int r = lane & 31, half = lane >> 5;
-    const int sw = (r >> 1) & 3;  // swz of every row this lane reads
+    const int sw = swz(r);  // swz of every row this lane reads (rows r + 32 i + 128 wi)
     a = (wi * 128 + r) * 64;
     b = HALF_BYTES + (wj * 128 + r) * 64;
     k0 = (half ^ sw) << 4;

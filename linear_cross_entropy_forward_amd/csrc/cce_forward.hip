@@ -3,14 +3,18 @@
 //
 // "Training — design (ORPO, flash-CCE head, …)" §5.1 and "ORPO training —
 // design", lever 1 "Implementation spec": for each vocab tile take the running
-// max m and sum s of exp(z - m), rescaling s when m grows; capture the target
-// logit where the target falls in the tile; lse = m + log s, logp = tgt - lse.
+// max m and sum s of exp(z - m), rescaling s when m grows; the target logit
+// h_i . W_{y_i}; lse = m + log s, logp = tgt - lse.
 //
 // Work split: workgroup (mt, split) owns 256 token rows and a contiguous run of
-// T vocab tiles of 256.  Each lane keeps (m, s) for the 4 tokens it owns across
-// all of its tiles; at the end the two lanes and two waves that share a token
-// merge, and the split writes one (m, s) pair per token into partials[S][Mpad].
-// A second kernel merges the S partials of a row in a fixed order, so results
+// T full vocab tiles of 256.  Each lane keeps (m, s) for the 4 tokens it owns
+// across all of its tiles; at the end the two lanes and two waves that share a
+// token merge, and the split writes one (m, s) pair per token into
+// partials[split][Mpad].  A ragged last vocab tile (V % 256 != 0) is handled
+// by a separate launch of the same kernel that masks the rows past V and
+// writes one more partial slot, so the main kernel carries no masking.  The
+// target logit is one dot product per row, computed by its own small kernel.
+// The merge kernel combines the partials of a row in a fixed order: results
 // are deterministic and nothing depends on atomics.
 #include "cce_device.hpp"
 #include "cce_launch.hpp"
@@ -21,25 +25,9 @@ namespace cce {
 // TAIL: the tile runs past V; entries with v >= V take no part.
 template <bool TAIL>
 __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int vw, int V, int half,
-                                                const int (&yj)[4], float (&m_run)[4],
-                                                float (&s_run)[4], float* __restrict__ tgt_row0,
-                                                int lane) {
+                                                float (&m_run)[4], float (&s_run)[4]) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    // target capture: the lane holding (token, y) stores the logit; rare, so
-    // the per-element compare runs only when some lane of the wave has a hit
-    const int off = yj[jj] - vw;
-    const bool hit = (unsigned)off < 128u && ((off >> 2) & 1) == half;
-    if (__ballot(hit) != 0ull) {
-      const int offh = off - 4 * half;
-      float tv = 0.f;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (offh == ii * 32 + 8 * (r >> 2) + (r & 3)) tv = acc[ii][jj][r];
-      if (hit) tgt_row0[jj * 32 + (lane & 31)] = tv;
-    }
     float mx = NEG_INF;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
@@ -49,58 +37,51 @@ __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int
         if (ok) mx = fmaxf(mx, acc[ii][jj][r]);
       }
     const float mn = fmaxf(m_run[jj], mx);
-    if (mn == NEG_INF) continue;
+    if (TAIL && mn == NEG_INF) continue;  // no valid entry yet for this lane
     const float nb = -mn * LOG2E;
     float sum = 0.f;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
         const float e = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nb));
-        if (ok) sum += e;
+        if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
       }
     s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
     m_run[jj] = mn;
   }
 }
 
-template <bool VEC, bool KTAIL>
+// Workgroup (mt, split) runs vocab tiles [t0 + split*T, min(t0 + (split+1)*T, t1))
+// and writes partial slot slot0 + split.
+template <bool VEC, bool KTAIL, bool TAIL>
 __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const u16* __restrict__ W,
-                                               const int* __restrict__ y, int M, int V, int D,
-                                               int nMt, int nVt, int S, int T, int nlaunch,
-                                               float* __restrict__ part_m, float* __restrict__ part_s,
-                                               float* __restrict__ tgt, int Mpad) {
+                                               int M, int V, int D, int nMt, int S, int T, int t0,
+                                               int t1, int slot0, int nlaunch,
+                                               float* __restrict__ part_m,
+                                               float* __restrict__ part_s, int Mpad) {
   __shared__ Smem sm;
   int mt, split;
   if (!map_tile(blockIdx.x, nlaunch, nMt, S, 8, mt, split)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
 
-  int yj[4];
   float m_run[4], s_run[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
-    yj[jj] = (j < M) ? y[j] : -1;
     m_run[jj] = NEG_INF;
     s_run[jj] = 0.f;
   }
   const u16* Hb = H + (size_t)mt * TILE * D;
   const int hrows = min(TILE, M - mt * TILE);
-  const int t_end = min((split + 1) * T, nVt);
-  float* tgt_row0 = tgt + mt * TILE + wj * 128;
+  const int t_end = min(t0 + (split + 1) * T, t1);
 
-  for (int t = split * T; t < t_end; ++t) {
+  for (int t = t0 + split * T; t < t_end; ++t) {
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    gemm_tile<VEC, false, KTAIL>(W + (size_t)v0 * D, D, min(TILE, V - v0), Hb, D, hrows, D, nullptr, 0, sm,
-                          acc);
-    const int vw = v0 + wi * 128;  // first vocab row of this wave's half of the tile
-    if (v0 + TILE > V)
-      fwd_tile_update<true>(acc, vw, V, half, yj, m_run, s_run, tgt_row0, lane);
-    else
-      fwd_tile_update<false>(acc, vw, V, half, yj, m_run, s_run, tgt_row0, lane);
+    gemm_tile<VEC, false, KTAIL>(W + (size_t)v0 * D, D, min(TILE, V - v0), Hb, D, hrows, D,
+                                 nullptr, 0, sm, acc);
+    fwd_tile_update<TAIL>(acc, v0 + wi * 128, V, half, m_run, s_run);
   }
 
   // lanes l and l^32 hold the same token: merge them
@@ -128,10 +109,34 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
       float m = m_run[jj], s = s_run[jj];
       lse_merge(m, s, xm[wj * 128 + jj * 32 + lane], xs[wj * 128 + jj * 32 + lane]);
       const int j = mt * TILE + wj * 128 + jj * 32 + lane;
-      part_m[(size_t)split * Mpad + j] = m;
-      part_s[(size_t)split * Mpad + j] = s;
+      part_m[(size_t)(slot0 + split) * Mpad + j] = m;
+      part_s[(size_t)(slot0 + split) * Mpad + j] = s;
     }
   }
+}
+
+// tgt[i] = h_i . W_{y_i} (fp32 sum of exact bf16 products), one wave per row.
+// Rows whose target is outside [0, V) are skipped (the merge reports them).
+__global__ __launch_bounds__(256) void k_target_logit(const u16* __restrict__ H,
+                                                      const u16* __restrict__ W,
+                                                      const int* __restrict__ y, int M, int V,
+                                                      int D, float* __restrict__ tgt) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int yy = y[row];
+  if (yy < 0 || yy >= V) return;
+  const u16* hr = H + (size_t)row * D;
+  const u16* wr = W + (size_t)yy * D;
+  float s = 0.f;
+  for (int k = lane; k < D; k += 64) {
+    const float a = __builtin_bit_cast(float, (unsigned)hr[k] << 16);
+    const float b = __builtin_bit_cast(float, (unsigned)wr[k] << 16);
+    s = fmaf(a, b, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) tgt[row] = s;
 }
 
 __global__ __launch_bounds__(256) void k_fwd_merge(const float* __restrict__ part_m,
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256) void k_fwd_merge(const float* __restrict__ par
   const int yy = y[j];
   unsigned err = 0u;
   if (yy >= 0 && yy < V) {
-    logp[j] = tgt[j] - L;
+    logp[j] = fminf(tgt[j] - L, 0.f);  // log of a probability; rounding can only push it above 0
   } else {
     logp[j] = 0.f;
     if (yy != -1) err |= 1u;  // CCE_DERR_TARGET
@@ -161,20 +166,38 @@ __global__ __launch_bounds__(256) void k_fwd_merge(const float* __restrict__ par
   if (err) atomicOr(status, err);
 }
 
-hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
-  const int n = a.nMt * a.S;
-  const int nlaunch = (n + 7) / 8 * 8;
-#define CCE_FWD(VEC, KT)                                                                          \
-  hipLaunchKernelGGL((k_fwd<VEC, KT>), dim3(nlaunch), dim3(NT), 0, st, a.H, a.W, a.y, a.M, a.V,     \
-                     a.D, a.nMt, a.nVt, a.S, a.T, nlaunch, a.part_m, a.part_s, a.tgt, a.Mpad)
+template <bool TAIL>
+static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int slot0,
+                             hipStream_t st) {
+  const int n = a.nMt * S;
+  const int nl = (n + 7) / 8 * 8;
+#define CCE_FWD(VEC, KT)                                                                         \
+  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D, \
+                     a.nMt, S, T, t0, t1, slot0, nl, a.part_m, a.part_s, a.Mpad)
   if (!a.vec) CCE_FWD(false, false);
   else if (a.D % BK != 0) CCE_FWD(true, true);
   else CCE_FWD(true, false);
 #undef CCE_FWD
+}
+
+hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
+  const int full = a.V / TILE;  // full vocab tiles
+  int slots = 0;
+  if (full > 0) {
+    launch_fwd_tiles<false>(a, a.S, a.T, 0, full, 0, st);
+    slots = a.S;
+  }
+  if (a.V % TILE != 0) {
+    launch_fwd_tiles<true>(a, 1, 1, full, full + 1, slots, st);
+    slots += 1;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_target_logit, dim3((a.M + 3) / 4), dim3(256), 0, st, a.H, a.W, a.y, a.M, a.V,
+                     a.D, a.tgt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, a.part_m, a.part_s,
-                     a.tgt, a.y, a.M, a.V, a.S, a.Mpad, a.logp, a.lse, a.status);
+                     a.tgt, a.y, a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status);
   return hipGetLastError();
 }
 

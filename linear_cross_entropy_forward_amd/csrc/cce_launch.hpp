@@ -60,6 +60,7 @@ struct BwdArgs {
   int M, V, D;
   int nMt, Mpad, Dpad, Vc;
   int ldM, ldV;  // row pitches (elements) of the M-long and Vc-long workspace rows
+  int ncu8;      // compute units rounded down to a multiple of 8 (persistent grids)
   bool vec;
   float filter_eps, block_eps;
   float* dh;
