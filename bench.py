@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
+    ap.add_argument("--v-sweep", action="store_true",
+                    help="time one step and record workspace / peak device memory at "
+                         "V in {32768, 65536, 131072, 262144} (M=8192, D=2560); one JSON line per V")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -110,8 +113,69 @@ def cpu_baseline(wl, rows: int):
                       f"D={wl.D}; fp64 forward+epilogue+backward; {dt:.2f} s"}
 
 
+def v_sweep(steps: int):
+    """Workspace and peak device memory against V at the Gemma-4B head's M and D.
+
+    Inputs and outputs grow with V (W, dW); the workspace must not.  Reported per
+    V: workspace bytes (what the library needs besides inputs and outputs), the
+    torch peak allocated during a step minus the inputs and outputs, and the
+    step time."""
+    import torch
+    from linear_cross_entropy_forward_amd import binding as B
+    from linear_cross_entropy_forward_amd import workloads as WL
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    torch.zeros(1, device=dev)  # initialise the context and the caching allocator
+    for V in (32768, 65536, 131072, 262144):
+        wl = WL.make_workload("gemma4b_head", V=V)
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base0 = torch.cuda.memory_allocated(dev)
+        h = B.to_device_bits(wl.h_bits, dev)
+        W = B.to_device_bits(wl.W_bits, dev)
+        y = torch.from_numpy(wl.y).to(dev)
+        seg = torch.from_numpy(wl.seg).to(dev)
+        dh = torch.empty((wl.M, wl.D), dtype=torch.float32, device=dev)
+        dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
+        logp = torch.empty(wl.M, dtype=torch.float32, device=dev)
+        lse = torch.empty_like(logp)
+        coef = torch.empty_like(logp)
+        out5 = torch.empty(5, dtype=torch.float32, device=dev)
+        pst = torch.empty((wl.n_pairs, 8), dtype=torch.float32, device=dev)
+        io_bytes = torch.cuda.memory_allocated(dev) - base0
+        head = B.Head(wl.M, wl.V, wl.D, dev)
+
+        def one():
+            head.forward(h, W, y, logp, lse)
+            head.epilogue(logp, y, seg, wl.n_pairs, wl.lam, wl.scope, out5, pst, coef)
+            head.backward(h, W, y, lse, coef, 0.0, 0.0, dh, dW)
+
+        for _ in range(2):
+            one()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            one()
+        e.record()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base0
+        rec = {"V": V, "M": wl.M, "D": wl.D, "workspace_bytes": B.workspace_bytes(wl.M, V, wl.D),
+               "inputs_outputs_bytes": io_bytes,
+               "peak_minus_inputs_outputs_bytes": peak - io_bytes,
+               "ms_per_step": round(s.elapsed_time(e) / steps, 3),
+               "tflops": round(8.0 * wl.M * V * wl.D / (s.elapsed_time(e) / steps * 1e-3) / 1e12, 1),
+               "status": head.read_status()}
+        print(json.dumps(rec), flush=True)
+        del h, W, y, seg, dh, dW, logp, lse, coef, out5, pst, head
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.v_sweep:
+        v_sweep(max(1, min(args.steps, 5)))
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic_json, args.workload)
         return

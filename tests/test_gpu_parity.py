@@ -266,6 +266,38 @@ def _sampled_full_size(name, device, n_rows=24):
     torch.cuda.empty_cache()
 
 
+def test_stress_filter_sampled(device):
+    """Stress config with its filter (eps 1e-5, response scope, lambda 0.5):
+    sampled dh rows against the oracle's filtered gradient (gated) and against
+    the exact one (reported)."""
+    wl = WL.make_workload("stress")
+    eps = wl.filter_eps
+    say(f"[gpu] stress filter eps={eps}: sampled rows")
+    head = B.Head(wl.M, wl.V, wl.D, device)
+    h, W, y, seg = upload(wl, device)
+    head.clear_status()
+    logp, lse = head.forward(h, W, y)
+    rng = np.random.default_rng(np.random.SeedSequence([WL.BASE_SEED, 78]))
+    coef = (rng.standard_normal(wl.M) * 1e-4).astype(np.float32)
+    coef[wl.y < 0] = 0.0
+    dh, dW = head.backward(h, W, y, lse, torch.from_numpy(coef).to(device), eps, eps)
+    torch.cuda.synchronize()
+    assert head.read_status() == 0
+    rows = np.sort(rng.choice(np.nonzero(coef != 0)[0], size=16, replace=False))
+    H64 = WL.bf16_bits_to_f32(wl.h_bits[rows]).astype(np.float64)
+    W64 = wl.W64()
+    _, lse_o = O.forward(H64, W64, wl.y[rows])
+    c = coef[rows].astype(np.float64)
+    dh_f = O.backward_dh_rows(H64, W64, wl.y[rows], lse_o, c, np.arange(16), filter_eps=eps)
+    dh_x = O.backward_dh_rows(H64, W64, wl.y[rows], lse_o, c, np.arange(16))
+    g = dh.cpu().numpy()[rows]
+    e_f, e_x = rel_l2(g, dh_f), rel_l2(g, dh_x)
+    say(f"  stress filter: vs filtered oracle {e_f:.3e}, vs exact {e_x:.3e}")
+    assert e_f <= RTOL_GRAD
+    del head, h, W, y, seg, logp, lse, dh, dW
+    torch.cuda.empty_cache()
+
+
 def _zero_head_full_size(name, device):
     """W = 0 at full size: lse = ln V, logp = -ln V, dh = 0 and
     dW_v = sum_i coef_i (1/V - [y_i = v]) h_i (closed form)."""
