@@ -65,11 +65,10 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.part_s = take((size_t)Scap * L.Mpad * sizeof(float));
   L.tgt = take((size_t)L.Mpad * sizeof(float));
   L.pairs = take((size_t)L.Mpad * cce::kPairStride * sizeof(double));
-  const int64_t ldM = L.Mpad + cce::kPitchPad, ldV = L.Vc + cce::kPitchPad;
-  L.ht = take((size_t)L.Dpad * ldM * 2);
-  L.wt = take((size_t)L.Dpad * ldV * 2);
-  L.g = take((size_t)L.Mpad * ldV * 2);
-  L.gt = take((size_t)L.Vc * ldM * 2);
+  L.ht = take((size_t)L.Dpad * L.Mpad * 2);
+  L.wt = take((size_t)L.Dpad * L.Vc * 2);
+  L.g = take((size_t)L.Mpad * L.Vc * 2);
+  L.gt = take((size_t)L.Vc * L.Mpad * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   L.total = off;
   return L;
@@ -221,8 +220,6 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.Mpad = (int)L.Mpad;
   a.Dpad = (int)L.Dpad;
   a.Vc = (int)L.Vc;
-  a.ldM = (int)L.Mpad + cce::kPitchPad;
-  a.ldV = (int)L.Vc + cce::kPitchPad;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
   a.filter_eps = filter_eps;
   a.block_eps = block_eps;

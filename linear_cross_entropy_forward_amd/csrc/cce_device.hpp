@@ -137,13 +137,20 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
 
-// Direct-to-LDS loads of one 256 x 32 K-slice of a row-major operand.  Wave w
-// moves rows 64w .. 64w+63 with 4 instructions of 16 rows; in each, lane L
-// fills LDS bytes 16L .. 16L+15 (row 16p + L/4 of the instruction, position
-// L%4), so it fetches global chunk (L%4) ^ swz(row).  The buffer resource ends
-// at row rows_valid: rows past it read as zero, and so does a chunk at k >= K
+// Direct-to-LDS loads of one 256 x 32 K-slice of an operand.  Wave w moves
+// rows 64w .. 64w+63 with 4 instructions of 16 rows; in each, lane L fills LDS
+// bytes 16L .. 16L+15 (row 16p + L/4 of the instruction, position L%4), so it
+// fetches global chunk (L%4) ^ swz(row).
+//
+// Row-major operand (leading dimension ld): the buffer resource ends at row
+// rows_valid, so rows past it read as zero, and so does a chunk at k >= K
 // (K tail, K % 8 == 0), which is pointed past the resource.
-template <bool KTAIL>
+//
+// BLOCKED operand: the tile is stored as K/32 consecutive 16 KB blocks, block b
+// holding rows 0..255 x K elements 32b .. 32b+31 row-major (64 bytes a row),
+// so each K-slice is one contiguous 16 KB read.  Every row is valid and
+// K % 32 == 0 (the workspace matrices the library writes itself).
+template <bool KTAIL, bool BLOCKED = false>
 struct DmaOperand {
   __amdgpu_buffer_rsrc_t rsrc;
   int voff;     // byte offset of this lane's chunk for instruction 0 at k = 0
@@ -152,22 +159,29 @@ struct DmaOperand {
   int K;
 
   __device__ __forceinline__ void init(const u16* base, int ld, int rows, int K_, int lane, int w) {
-    rsrc = make_rsrc(base, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld * 2u);
     // row bits 0..3 are lane bits 2..5, so swz(row) = swz(lane >> 2) for every instruction
     const int c = (lane & 3) ^ swz(lane >> 2);
     const int row0 = 64 * w + (lane >> 2);
-    voff = row0 * ld * 2 + c * 16;
-    pstride = 16 * ld * 2;
+    if (BLOCKED) {
+      rsrc = make_rsrc(base, (unsigned)(K_ >> 5) * 16384u);
+      voff = row0 * 64 + c * 16;
+      pstride = 16 * 64;
+    } else {
+      rsrc = make_rsrc(base, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld * 2u);
+      voff = row0 * ld * 2 + c * 16;
+      pstride = 16 * ld * 2;
+    }
     c8 = c * 8;
     K = K_;
   }
 
   // Issue the 4 loads of K-slice k0 into the operand region `dst` of a stage.
   __device__ __forceinline__ void issue(int k0, unsigned char* dst, int w) const {
-    const bool kv = !KTAIL || k0 + c8 < K;
+    const bool kv = BLOCKED || !KTAIL || k0 + c8 < K;
+    const int kb = BLOCKED ? k0 * 512 : k0 * 2;  // bytes to slice k0 (a 16 KB block per 32 of K)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int off = kv ? voff + p * pstride + k0 * 2 : 0x7ffffff0;
+      const int off = kv ? voff + p * pstride + kb : 0x7ffffff0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, to_lds(dst + (64 * w + 16 * p) * 64), 16, off,
                                                0, 0, 0);
     }
@@ -265,7 +279,9 @@ __device__ __forceinline__ void ring_barrier() {
   }
 
 // acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles at A and B
-// (leading dimensions lda, ldb; rows beyond a_rows / b_rows are zero).
+// (leading dimensions lda, ldb; rows beyond a_rows / b_rows are zero; with
+// BLOCKED both tiles are in the blocked layout of DmaOperand and lda / ldb /
+// a_rows / b_rows are unused).
 // SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive; its
 // MFMAs are skipped (its slices still stream through LDS).
 //
@@ -279,7 +295,7 @@ __device__ __forceinline__ void ring_barrier() {
 //     fragments
 // Slices past the last one are clamped to it (their stages are no longer
 // read); the loop ends by draining every load and a barrier, so LDS is free.
-template <bool VEC, bool SKIP, bool KTAIL>
+template <bool VEC, bool SKIP, bool KTAIL, bool BLOCKED = false>
 __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, int a_rows,
                                           const u16* __restrict__ B, int ldb, int b_rows, int K,
                                           const int* __restrict__ kflags, int kflag_stride,
@@ -294,7 +310,7 @@ __device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, in
   unsigned char* ring = sm.raw;
   const int nk = (K + BK - 1) / BK;
   if (VEC) {
-    DmaOperand<KTAIL> da, db;
+    DmaOperand<KTAIL, BLOCKED> da, db;
     da.init(A, lda, a_rows, K, lane, w);
     db.init(B, ldb, b_rows, K, lane, w);
     const int klast = (nk - 1) * BK;

@@ -15,10 +15,6 @@ constexpr int kTile = 256;
 constexpr int kVocabChunk = 16384;
 // Doubles per pair in the epilogue's pair table.
 constexpr int kPairStride = 16;
-// Extra bf16 elements per row of every backward workspace matrix: keeps row
-// pitches off powers of two, so the rows one load or store instruction
-// touches spread over the memory channels.
-constexpr int kPitchPad = 64;
 
 struct FwdArgs {
   const u16* H;
@@ -59,16 +55,17 @@ struct BwdArgs {
   const float* coef;
   int M, V, D;
   int nMt, Mpad, Dpad, Vc;
-  int ldM, ldV;  // row pitches (elements) of the M-long and Vc-long workspace rows
   int ncu8;      // compute units rounded down to a multiple of 8 (persistent grids)
   bool vec;
   float filter_eps, block_eps;
   float* dh;
   float* dW;
-  u16* HT;     // [Dpad, Mpad], pitch ldM
-  u16* WT;     // [Dpad, Vc], pitch ldV
-  u16* G;      // [Mpad, Vc], pitch ldV
-  u16* GT;     // [Vc, Mpad], pitch ldM
+  // bf16 workspace matrices in the blocked layout (256-row tiles, each a run
+  // of K/32 blocks of 256 x 32 elements):
+  u16* HT;     // [Dpad, Mpad]
+  u16* WT;     // [Dpad, Vc]
+  u16* G;      // [Mpad, Vc]
+  u16* GT;     // [Vc, Mpad]
   int* flags;  // [nMt, Vc / kTile]
   unsigned* status;
 };
