@@ -45,7 +45,7 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
-  size_t part_m, part_s, tgt, pairs, ht, wt, g, gt, flags, total;
+  size_t part_m, part_s, tgt, pairs, g, flags, total;
 };
 
 Layout layout(int64_t M, int64_t V, int64_t D) {
@@ -65,10 +65,7 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.part_s = take((size_t)Scap * L.Mpad * sizeof(float));
   L.tgt = take((size_t)L.Mpad * sizeof(float));
   L.pairs = take((size_t)L.Mpad * cce::kPairStride * sizeof(double));
-  L.ht = take((size_t)L.Dpad * L.Mpad * 2);
-  L.wt = take((size_t)L.Dpad * L.Vc * 2);
   L.g = take((size_t)L.Mpad * L.Vc * 2);
-  L.gt = take((size_t)L.Vc * L.Mpad * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   L.total = off;
   return L;
@@ -225,10 +222,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.block_eps = block_eps;
   a.dh = dh;
   a.dW = dW;
-  a.HT = reinterpret_cast<cce::u16*>(base + L.ht);
-  a.WT = reinterpret_cast<cce::u16*>(base + L.wt);
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
-  a.GT = reinterpret_cast<cce::u16*>(base + L.gt);
   a.flags = reinterpret_cast<int*>(base + L.flags);
   a.status = dev_status;
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK

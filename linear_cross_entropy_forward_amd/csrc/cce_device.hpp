@@ -40,11 +40,9 @@ constexpr int NT = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-// The operand ring (4 x 32 KB) and, after the K loop, epilogue staging of up
-// to 256 x 264 bf16.
+// The operand ring (4 x 32 KB); epilogues reuse it after the K loop.
 struct __align__(16) Smem {
-  unsigned char raw[NSTAGE * STAGE_BYTES > TILE * (TILE + 8) * 2 ? NSTAGE * STAGE_BYTES
-                                                                 : TILE * (TILE + 8) * 2];
+  unsigned char raw[NSTAGE * STAGE_BYTES];
 };
 
 // ---------------------------------------------------------------------------
@@ -104,18 +102,22 @@ __device__ __forceinline__ bool map_tile(int bid, int nlaunch, int nA, int nB, i
   return true;
 }
 
-// Buffer resource over [base, base + bytes): loads whose (range-checked) VGPR
-// offset falls past the end return zero.  The scalar offset is always 0.
-// base and bytes are workgroup-uniform (kernel arguments and blockIdx only);
-// readfirstlane states that, so the descriptor lives in SGPRs and the loads
-// need no per-lane waterfall loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+// Buffer descriptor over [base, base + bytes), as the 4 dwords the buffer
+// instructions take: 48-bit base, stride 0 (raw buffer: offsets are bytes),
+// num_records = bytes, and dword 3 = 32-bit data format (untyped loads ignore
+// it).  Loads whose range-checked VGPR offset falls past the end return zero.
+// base and bytes are workgroup-uniform (kernel arguments, blockIdx and loop
+// counters only); readfirstlane states that, so the descriptor lives in SGPRs
+// and the loads need no per-lane waterfall loop.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
-  void* pu = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           0x00020000);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((unsigned)(p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -137,102 +139,265 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
 
-// Direct-to-LDS loads of one 256 x 32 K-slice of an operand.  Wave w moves
-// rows 64w .. 64w+63 with 4 instructions of 16 rows; in each, lane L fills LDS
-// bytes 16L .. 16L+15 (row 16p + L/4 of the instruction, position L%4), so it
-// fetches global chunk (L%4) ^ swz(row).
-//
-// Row-major operand (leading dimension ld): the buffer resource ends at row
-// rows_valid, so rows past it read as zero, and so does a chunk at k >= K
-// (K tail, K % 8 == 0), which is pointed past the resource.
-//
-// BLOCKED operand: the tile is stored as K/32 consecutive 16 KB blocks, block b
-// holding rows 0..255 x K elements 32b .. 32b+31 row-major (64 bytes a row),
-// so each K-slice is one contiguous 16 KB read.  Every row is valid and
-// K % 32 == 0 (the workspace matrices the library writes itself).
-template <bool KTAIL, bool BLOCKED = false>
-struct DmaOperand {
-  __amdgpu_buffer_rsrc_t rsrc;
-  int voff;     // byte offset of this lane's chunk for instruction 0 at k = 0
-  int pstride;  // bytes between instructions (16 rows)
-  int c8;       // this lane's chunk index * 8 (K elements)
-  int K;
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(void* p) {
+  return (unsigned)(uintptr_t)(lds_ptr_t)(p);
+}
 
-  __device__ __forceinline__ void init(const u16* base, int ld, int rows, int K_, int lane, int w) {
-    // row bits 0..3 are lane bits 2..5, so swz(row) = swz(lane >> 2) for every instruction
-    const int c = (lane & 3) ^ swz(lane >> 2);
-    const int row0 = 64 * w + (lane >> 2);
-    if (BLOCKED) {
-      rsrc = make_rsrc(base, (unsigned)(K_ >> 5) * 16384u);
-      voff = row0 * 64 + c * 16;
-      pstride = 16 * 64;
-    } else {
-      rsrc = make_rsrc(base, (unsigned)(rows > 0 ? rows : 0) * (unsigned)ld * 2u);
-      voff = row0 * ld * 2 + c * 16;
-      pstride = 16 * ld * 2;
-    }
-    c8 = c * 8;
+// One direct-to-LDS load (buffer_load_dwordx4 ... lds): lane L's 16 bytes at
+// buffer offset voff land at LDS byte m0 + 16 L (m0 wave-uniform).  It is
+// written as assembly so that the compiler does not count it as an LDS store:
+// otherwise every LDS read it cannot prove disjoint from the stage being
+// filled gets a wait for ALL loads in flight, which drains the operand
+// pipeline each K step.  The order between these loads and the LDS reads of
+// their data is kept explicitly (CCE_WAIT_VMCNT, then a barrier).  s_nop
+// covers the M0 write-to-use hazard.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, unsigned m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(m0)
+               : "m0");
+}
+
+// ---------------------------------------------------------------------------
+// Operand storage.  The core contracts two 256-row operand tiles over K; each
+// operand is read from global memory in one of four forms:
+//
+//   OP_ROW   row-major [i][k] (K contiguous), leading dimension ld; rows
+//            i >= rows read as zero, and so does a K tail (K % 8 == 0)
+//   OP_BLK   one blocked tile: K/32 consecutive 16 KB blocks, block b holding
+//            rows 0..255 x k = 32b .. 32b+31 row-major (64 bytes a row);
+//            K % 32 == 0, every row valid (workspace the library writes)
+//   OP_KROW  the operand transposed, row-major [k][i] with pitch ld: element
+//            (i, k) at base[k * ld + i]; k >= rows or i >= cols read as zero
+//   OP_KBLK  the operand is the transpose of a blocked matrix X (256 x 32
+//            blocks, ld = blocks per 256-row tile of X): i runs over the 256
+//            columns of one column tile of X (base points at its first block),
+//            k over the rows of X
+//
+// Row forms land in LDS as [256 rows][64 bytes] with 16-byte chunk c of row r
+// at position c ^ swz(r) (above).  K forms land as [32 k-rows][512 bytes]:
+// chunk c (i = 8c .. 8c+7) of k-row kr at position c ^ kswz(kr), and their
+// MFMA fragments are read with the transposing LDS read (ds_read_b64_tr_b16).
+// ---------------------------------------------------------------------------
+enum : int { OP_ROW = 0, OP_BLK = 1, OP_KROW = 2, OP_KBLK = 3 };
+
+// Chunk swizzle of the K forms, by k-row modulo 4: 0, 6, 12, 10.  The
+// transposing fragment read makes each 16-lane group read 4 consecutive
+// k-rows x 32 bytes (and each 32 lanes 4 k-rows x 64 bytes); this XOR puts
+// those pieces in distinct banks for 32 or 64 banks of 4 bytes.
+__device__ __forceinline__ int kswz(int kr) { return (0xAC60 >> (4 * (kr & 3))) & 15; }
+
+struct OpRef {
+  const u16* p;
+  int ld, rows, cols;
+};
+
+// Direct-to-LDS loads of one K-slice of an operand: wave w issues 4
+// instructions p, each filling 1 KB of the operand's 16 KB stage region; lane
+// L of instruction p writes LDS bytes (64w + 16p) * 64 + 16 L and chooses its
+// global chunk so that the layouts above come out.
+//   row forms: row 64w + 16p + L/4, position L%4 -> chunk (L%4) ^ swz(row)
+//   K forms:   k-row 8w + 2p + L/32, position L%32 -> chunk (L%32) ^ kswz(k-row)
+// Loads past a buffer resource's end read zero; an invalid chunk is pointed
+// past the end.  K forms rebase their resource every slice so that no offset
+// exceeds 32 bits whatever the matrix size.
+template <int MODE, bool KTAIL>
+struct DmaOperand {
+  i32x4 rsrc;  // row forms: over the whole tile
+  const u16* base;
+  int ld, rows;
+  int voff[2];  // byte offset of this lane's chunk (row forms: [0]; K forms: even / odd p)
+  int pstride;  // bytes between instructions (row forms) or instruction pairs (K forms)
+  int c8;       // row forms: this lane's chunk index * 8 (K elements)
+  int K;
+  unsigned ldsw;  // LDS bytes before this wave's first instruction (4 KB per wave)
+
+  __device__ __forceinline__ void init(const OpRef& op, int K_, int lane, int w) {
+    base = op.p;
+    ld = op.ld;
+    rows = op.rows;
     K = K_;
+    ldsw = (unsigned)__builtin_amdgcn_readfirstlane(w * 4096);
+    if (MODE == OP_ROW || MODE == OP_BLK) {
+      // row bits 0..3 are lane bits 2..5, so swz(row) = swz(lane >> 2) for every instruction
+      const int c = (lane & 3) ^ swz(lane >> 2);
+      const int row0 = 64 * w + (lane >> 2);
+      if (MODE == OP_BLK) {
+        rsrc = make_rsrc(op.p, (unsigned)(K_ >> 5) * 16384u);
+        voff[0] = row0 * 64 + c * 16;
+        pstride = 16 * 64;
+      } else {
+        rsrc = make_rsrc(op.p, (unsigned)(op.rows > 0 ? op.rows : 0) * (unsigned)op.ld * 2u);
+        voff[0] = row0 * op.ld * 2 + c * 16;
+        pstride = 16 * op.ld * 2;
+      }
+      voff[1] = 0;
+      c8 = c * 8;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kr = 8 * w + 2 * e + (lane >> 5);
+        const int c = (lane & 31) ^ kswz(kr);
+        if (MODE == OP_KROW)
+          voff[e] = 8 * c < op.cols ? kr * op.ld * 2 + c * 16 : 0x40000000;
+        else
+          voff[e] = (c >> 2) * 16384 + kr * 64 + (c & 3) * 16;
+      }
+      pstride = MODE == OP_KROW ? 4 * op.ld * 2 : 4 * 64;  // instructions p and p+2: 4 k-rows
+      c8 = 0;
+    }
   }
 
-  // Issue the 4 loads of K-slice k0 into the operand region `dst` of a stage.
-  __device__ __forceinline__ void issue(int k0, unsigned char* dst, int w) const {
-    const bool kv = BLOCKED || !KTAIL || k0 + c8 < K;
-    const int kb = BLOCKED ? k0 * 512 : k0 * 2;  // bytes to slice k0 (a 16 KB block per 32 of K)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int off = kv ? voff + p * pstride + kb : 0x7ffffff0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, to_lds(dst + (64 * w + 16 * p) * 64), 16, off,
-                                               0, 0, 0);
+  // Per-slice state of K-slice k0: the buffer resource the slice's loads use
+  // (row forms: the tile's; K forms: rebased at the slice) and, for row
+  // forms, whether this lane's chunk is inside K.
+  struct Slice {
+    i32x4 rs;
+    int kb;  // bytes added to every offset
+    bool kv;
+  };
+  __device__ __forceinline__ Slice slice(int k0) const {
+    Slice sl;
+    if (MODE == OP_ROW || MODE == OP_BLK) {
+      sl.rs = rsrc;
+      sl.kb = MODE == OP_BLK ? k0 * 512 : k0 * 2;
+      sl.kv = MODE == OP_BLK || !KTAIL || k0 + c8 < K;
+    } else {
+      const u16* sb;
+      unsigned nbytes;
+      if (MODE == OP_KROW) {
+        const int nr = rows - k0;
+        sb = base + (size_t)k0 * ld;
+        nbytes = nr <= 0 ? 0u : (unsigned)(nr < BK ? nr : BK) * (unsigned)ld * 2u;
+      } else {
+        sb = base + (size_t)(k0 >> 8) * ld * 8192 + (size_t)(k0 & 255) * 32;
+        nbytes = 8u * 16384u;
+      }
+      sl.rs = make_rsrc(sb, nbytes);
+      sl.kb = 0;
+      sl.kv = true;
     }
+    return sl;
+  }
+
+  // Load instruction p (0..3) of a slice into the operand region of a stage at
+  // LDS byte address dst.
+  __device__ __forceinline__ void issue(const Slice& sl, unsigned dst, int p) const {
+    int off;
+    if (MODE == OP_ROW || MODE == OP_BLK)
+      off = sl.kv ? voff[0] + p * pstride + sl.kb : 0x7ffffff0;
+    else
+      off = voff[p & 1] + (p >> 1) * pstride;
+    dma16(sl.rs, off, dst + ldsw + p * 1024);
+  }
+
+  // All 4 loads of K-slice k0.
+  __device__ __forceinline__ void issue_all(int k0, unsigned dst) const {
+    const Slice sl = slice(k0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue(sl, dst, p);
   }
 };
 
-// Element-by-element loads of one K-slice into the same swizzled layout (the
-// path for odd D or 16-byte-misaligned operands; not pipelined).
-__device__ __forceinline__ void slow_slice(const u16* __restrict__ base, int ld, int rows_valid,
-                                           int K, int k0, unsigned char* dst, int tid) {
+// Element (i, k) of an operand in any of the forms (the unvectorised path).
+template <int MODE>
+__device__ __forceinline__ unsigned op_elem(const OpRef& op, int K, int i, int k) {
+  if (MODE == OP_ROW) return (i < op.rows && k < K) ? op.p[(size_t)i * op.ld + k] : 0u;
+  if (MODE == OP_BLK) return op.p[(size_t)(k >> 5) * 8192 + i * 32 + (k & 31)];
+  if (MODE == OP_KROW) return (k < op.rows && i < op.cols) ? op.p[(size_t)k * op.ld + i] : 0u;
+  return op.p[((size_t)(k >> 8) * op.ld + (i >> 5)) * 8192 + (k & 255) * 32 + (i & 31)];
+}
+
+// Element-by-element loads of one K-slice into the same LDS layout (the path
+// for odd D or 16-byte-misaligned operands; not pipelined).
+template <int MODE>
+__device__ __forceinline__ void slow_slice(const OpRef& op, int K, int k0, unsigned char* dst,
+                                           int tid) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int idx = tid + 256 * p;  // 1024 chunks: row idx/4, chunk idx%4
-    const int row = idx >> 2, c = idx & 3;
-    const int k = k0 + c * 8;
+    const int idx = tid + 256 * p;  // 1024 chunks of 16 bytes
     unsigned e[8];
+    int at;
+    if (MODE == OP_ROW || MODE == OP_BLK) {
+      const int row = idx >> 2, c = idx & 3;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      e[q] = (row < rows_valid && k + q < K) ? base[(size_t)row * ld + k + q] : 0u;
-    *reinterpret_cast<u32x4*>(dst + row * 64 + ((c ^ swz(row)) << 4)) =
+      for (int q = 0; q < 8; ++q) e[q] = op_elem<MODE>(op, K, row, k0 + 8 * c + q);
+      at = row * 64 + ((c ^ swz(row)) << 4);
+    } else {
+      const int kr = idx >> 5, c = idx & 31;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e[q] = op_elem<MODE>(op, K, 8 * c + q, k0 + kr);
+      at = kr * 512 + ((c ^ kswz(kr)) << 4);
+    }
+    *reinterpret_cast<u32x4*>(dst + at) =
         u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
   }
 }
 
 // Fragments of one 16-wide K sub-step: 4 A tiles and 4 B tiles of 32 rows.
+// Lane l holds row l%32 of its tile, K elements 8*(l/32) .. 8*(l/32)+7.
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
-// Per-lane byte offsets of the fragment rows inside a stage.
+// Per-lane byte offsets of the fragments inside a stage.
+//   row forms: a / b = row part (tile 0); k0 / k1 = chunk part of sub-step 0 / 1
+//   K forms:   a / b = address of tile 0, sub-step 0; tile t is at a ^ (t << 6)
+//              (the chunk bits the tile index occupies), sub-step 1 at +8192
+// K forms, transposing read: in each 16-lane group, source lane s points at
+// k-row kr0 + s/4 and i = i0 + 4*(s%4); lane s then receives element
+// (i0 + s, kr0 .. kr0+3).  Two reads, 4 k-rows apart, give the lane's 8 K
+// elements.  Lanes 16..31 take i0 + 16, lanes 32..63 take K elements 8..15.
+template <bool AK, bool BKM>
 struct FragAddr {
-  int a, b;    // row part of the A / B addresses (tile 0)
-  int k0, k1;  // chunk part for sub-step 0 (K 0..15) and sub-step 1 (K 16..31)
+  int a, b;
+  int k0, k1;
   __device__ __forceinline__ void init(int lane, int wi, int wj) {
     const int r = lane & 31, half = lane >> 5;
     const int sw = swz(r);  // swz of every row this lane reads (rows r + 32 i + 128 wi)
-    a = (wi * 128 + r) * 64;
-    b = HALF_BYTES + (wj * 128 + r) * 64;
     k0 = (half ^ sw) << 4;
     k1 = ((2 + half) ^ sw) << 4;
+    const int s = lane & 15, gi = (lane >> 4) & 1;
+    const int kr = 8 * half + (s >> 2);
+    const int kbase = kr * 512 + (((2 * gi + ((s >> 1) & 1)) ^ kswz(kr)) << 4) + 8 * (s & 1);
+    a = AK ? kbase + wi * 256 : (wi * 128 + r) * 64;
+    b = HALF_BYTES + (BKM ? kbase + wj * 256 : (wj * 128 + r) * 64);
   }
 };
 
-__device__ __forceinline__ void load_frags(const unsigned char* stage, const FragAddr& fa, int kpart,
-                                           Frags& f) {
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ bf16x8 read_tr_frag(const unsigned char* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Fragment i of the A (B) operand for sub-step `sub` of the stage at `stage`.
+template <bool AK, bool BKM>
+__device__ __forceinline__ bf16x8 frag_a(const unsigned char* stage, const FragAddr<AK, BKM>& fa,
+                                         int sub, int i) {
+  return AK ? read_tr_frag(stage + ((fa.a ^ (i << 6)) + sub * 8192))
+            : *reinterpret_cast<const bf16x8*>(stage + fa.a + i * 32 * 64 + (sub ? fa.k1 : fa.k0));
+}
+template <bool AK, bool BKM>
+__device__ __forceinline__ bf16x8 frag_b(const unsigned char* stage, const FragAddr<AK, BKM>& fa,
+                                         int sub, int j) {
+  return BKM ? read_tr_frag(stage + ((fa.b ^ (j << 6)) + sub * 8192))
+             : *reinterpret_cast<const bf16x8*>(stage + fa.b + j * 32 * 64 + (sub ? fa.k1 : fa.k0));
+}
+
+template <bool AK, bool BKM>
+__device__ __forceinline__ void load_frags(const unsigned char* stage, const FragAddr<AK, BKM>& fa,
+                                           int sub, Frags& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const bf16x8*>(stage + fa.a + i * 32 * 64 + kpart);
+  for (int i = 0; i < 4; ++i) f.a[i] = frag_a(stage, fa, sub, i);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.b[j] = *reinterpret_cast<const bf16x8*>(stage + fa.b + j * 32 * 64 + kpart);
+  for (int j = 0; j < 4; ++j) f.b[j] = frag_b(stage, fa, sub, j);
 }
 
 __device__ __forceinline__ void mma_16(const Frags& f, floatx16 (&acc)[4][4]) {
@@ -252,10 +417,10 @@ __device__ __forceinline__ void zero_acc(floatx16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
-#define CCE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+// Wait until at most n vector-memory operations of this wave are in flight
+// (n a literal).  Assembly, so that the compiler neither drops nor merges it:
+// it does not see the direct-to-LDS loads this wait is for.
+#define CCE_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
 // Workgroup barrier for the operand ring: waits for this wave's LDS reads
 // (lgkmcnt 0) but not for its in-flight direct-to-LDS loads; the caller has
@@ -269,94 +434,161 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Scheduling hints: interleave `n` instructions of class `mask` one by one
-// with MFMAs, so that in-order issue never blocks the MFMA pipe behind a burst
-// of memory instructions.  (mask: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read.)
-#define CCE_INTERLEAVE(mask, n)                           \
-  _Pragma("unroll") for (int _q = 0; _q < (n); ++_q) {    \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    \
-    __builtin_amdgcn_sched_group_barrier((mask), 1, 0);   \
-  }
 
-// acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles at A and B
-// (leading dimensions lda, ldb; rows beyond a_rows / b_rows are zero; with
-// BLOCKED both tiles are in the blocked layout of DmaOperand and lda / ldb /
-// a_rows / b_rows are unused).
+// Fragment r (0..7) of a sub-step in the order the next sub-step's MFMAs
+// consume them: A0, B0, B1, B2, B3, A1, A2, A3.
+template <bool AK, bool BKM>
+__device__ __forceinline__ void read_frag(const unsigned char* stage, const FragAddr<AK, BKM>& fa,
+                                          int sub, int r, Frags& f) {
+  if (r == 0) f.a[0] = frag_a(stage, fa, sub, 0);
+  else if (r < 5) f.b[r - 1] = frag_b(stage, fa, sub, r - 1);
+  else f.a[r - 4] = frag_a(stage, fa, sub, r - 4);
+}
+
+// One K step of the pipelined loop (slice kt in stage `cur`; `nxt` holds slice
+// kt+1; `far` receives slice kt+3), in a fixed instruction order:
+//   sub-step 0: 16 MFMAs (A tile i = q/4, B tile j = q%4) on fragments read
+//     earlier; after MFMA q comes, for even q, direct-to-LDS load q/2 of
+//     slice kt+3 into `far` (A, then B; `far` was last read in iteration
+//     kt-1, before the barrier that ended it) and, for odd q, the LDS read of
+//     one of sub-step 1's fragments
+//   wait until this wave's loads of slice kt+1 have landed, then barrier
+//   sub-step 1: 16 MFMAs; after each of the first 8, the read of one of slice
+//     kt+1's first fragments.
+// sched_barrier pins the order: one memory instruction between MFMAs keeps
+// the in-order issue from stalling the MFMA pipe behind a burst of them.
+template <int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
+__device__ __forceinline__ void gemm_step(const DmaOperand<AMODE, KTAIL>& da,
+                                          const DmaOperand<BMODE, KTAIL>& db,
+                                          const FragAddr<AK, BKM>& fa, int kn,
+                                          const unsigned char* cur, const unsigned char* nxt,
+                                          unsigned far, Frags& f0, Frags& f1,
+                                          floatx16 (&acc)[4][4]) {
+  const typename DmaOperand<AMODE, KTAIL>::Slice sa = da.slice(kn);
+  const typename DmaOperand<BMODE, KTAIL>::Slice sb = db.slice(kn);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
+    if ((q & 1) == 0) {
+      if (q < 8) da.issue(sa, far, q >> 1);
+      else db.issue(sb, far + HALF_BYTES, (q >> 1) - 4);
+    } else {
+      read_frag(cur, fa, 1, q >> 1, f1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slices kt+2, kt+3 may be in flight)
+  ring_barrier();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
+    if (q < 8) read_frag(nxt, fa, 0, q, f0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The pipelined K loop over the 4 ring stages at `ring` (LDS byte address
+// ring_lds), unrolled by 4 so that every access names its stage statically
+// (constant LDS offsets).  The order between the direct-to-LDS loads and the
+// reads of their data is kept by the explicit vmcnt waits and barriers only.
+// SKIP: a slice whose 256-wide K block is flagged inactive streams through
+// the ring without its MFMAs.  This variant branches around each sub-step's
+// 16 MFMAs as a whole (no interleaving, no unrolling): control flow between
+// interleaved MFMAs leaves the register allocator unable to keep the
+// accumulators in place.
+template <bool SKIP, int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
+__device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
+                                          const DmaOperand<BMODE, KTAIL>& db,
+                                          const FragAddr<AK, BKM>& fa, int nk,
+                                          const int* __restrict__ kflags, int kflag_stride,
+                                          const unsigned char* ring, unsigned ring_lds,
+                                          floatx16 (&acc)[4][4]) {
+  const int klast = (nk - 1) * BK;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int k = min(s * BK, klast);
+    da.issue_all(k, ring_lds + s * STAGE_BYTES);
+    db.issue_all(k, ring_lds + s * STAGE_BYTES + HALF_BYTES);
+  }
+  CCE_WAIT_VMCNT(16);  // slice 0 landed (slices 1 and 2 may be in flight)
+  ring_barrier();
+  Frags f0, f1;
+  load_frags(ring, fa, 0, f0);
+  if (SKIP) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const unsigned char* cur = ring + (kt & 3) * STAGE_BYTES;
+      const unsigned char* nxt = ring + ((kt + 1) & 3) * STAGE_BYTES;
+      const unsigned far = ring_lds + ((kt + 3) & 3) * STAGE_BYTES;
+      const bool active = kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
+      const int kn = min((kt + 3) * BK, klast);
+      da.issue_all(kn, far);
+      db.issue_all(kn, far + HALF_BYTES);
+      load_frags(cur, fa, 1, f1);
+      if (active) mma_16(f0, acc);
+      CCE_WAIT_VMCNT(16);
+      ring_barrier();
+      load_frags(nxt, fa, 0, f0);
+      if (active) mma_16(f1, acc);
+    }
+    CCE_WAIT_VMCNT(0);
+    __syncthreads();
+    return;
+  }
+  for (int kt0 = 0; kt0 < nk; kt0 += NSTAGE) {
+#pragma unroll
+    for (int j = 0; j < NSTAGE; ++j) {
+      const int kt = kt0 + j;
+      if (kt < nk)
+        gemm_step(da, db, fa, min((kt + 3) * BK, klast), ring + j * STAGE_BYTES,
+                  ring + ((j + 1) & 3) * STAGE_BYTES, ring_lds + ((j + 3) & 3) * STAGE_BYTES, f0,
+                  f1, acc);
+    }
+  }
+  CCE_WAIT_VMCNT(0);
+  __syncthreads();
+}
+
+// acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles A and B, each in
+// the form AMODE / BMODE (KTAIL: a row-form operand may end inside a K-slice).
 // SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive; its
 // MFMAs are skipped (its slices still stream through LDS).
-//
-// VEC path, iteration kt (slice kt sits in stage kt % 4):
-//   issue the direct-to-LDS loads of slice kt+3 into stage (kt+3) % 4 (last
-//     read in iteration kt-1, before the barrier that ended it)
-//   sub-step 0: 16 MFMAs on fragments read earlier, interleaved with those
-//     loads and the LDS reads of sub-step 1's fragments
-//   wait until this wave's loads of slice kt+1 have landed, then barrier
-//   sub-step 1: 16 MFMAs interleaved with the reads of slice kt+1's first
-//     fragments
-// Slices past the last one are clamped to it (their stages are no longer
-// read); the loop ends by draining every load and a barrier, so LDS is free.
-template <bool VEC, bool SKIP, bool KTAIL, bool BLOCKED = false>
-__device__ __forceinline__ void gemm_tile(const u16* __restrict__ A, int lda, int a_rows,
-                                          const u16* __restrict__ B, int ldb, int b_rows, int K,
+// VEC: the pipelined loop above (slice kt sits in stage kt % 4; slices past
+// the last one are clamped to it, their stages no longer read); it ends by
+// draining every load and a barrier, so LDS is free.  Otherwise one slice at
+// a time through element loads.
+template <bool VEC, bool SKIP, bool KTAIL, int AMODE = OP_ROW, int BMODE = OP_ROW>
+__device__ __forceinline__ void gemm_tile(const OpRef& A, const OpRef& B, int K,
                                           const int* __restrict__ kflags, int kflag_stride,
                                           Smem& sm, floatx16 (&acc)[4][4]) {
+  constexpr bool AK = AMODE >= OP_KROW, BKM = BMODE >= OP_KROW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int wi = w & 1, wj = w >> 1;
   zero_acc(acc);
-  FragAddr fa;
+  FragAddr<AK, BKM> fa;
   fa.init(lane, wi, wj);
   unsigned char* ring = sm.raw;
   const int nk = (K + BK - 1) / BK;
   if (VEC) {
-    DmaOperand<KTAIL, BLOCKED> da, db;
-    da.init(A, lda, a_rows, K, lane, w);
-    db.init(B, ldb, b_rows, K, lane, w);
-    const int klast = (nk - 1) * BK;
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s) {
-      const int k = min(s * BK, klast);
-      da.issue(k, ring + s * STAGE_BYTES, w);
-      db.issue(k, ring + s * STAGE_BYTES + HALF_BYTES, w);
-    }
-    CCE_WAIT_VMCNT(16);  // slice 0 landed (slices 1 and 2 may be in flight)
-    ring_barrier();
-    Frags f0, f1;
-    load_frags(ring, fa, fa.k0, f0);
-    for (int kt = 0; kt < nk; ++kt) {
-      unsigned char* cur = ring + (kt & (NSTAGE - 1)) * STAGE_BYTES;
-      unsigned char* nxt = ring + ((kt + 1) & (NSTAGE - 1)) * STAGE_BYTES;
-      unsigned char* far = ring + ((kt + 3) & (NSTAGE - 1)) * STAGE_BYTES;
-      const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
-      // sub-step 0
-      const int kn = min((kt + 3) * BK, klast);
-      da.issue(kn, far, w);
-      db.issue(kn, far + HALF_BYTES, w);
-      load_frags(cur, fa, fa.k1, f1);
-      if (active) mma_16(f0, acc);
-      CCE_INTERLEAVE(0x020, 8)
-      CCE_INTERLEAVE(0x100, 8)
-      CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slices kt+2, kt+3 may be in flight)
-      ring_barrier();
-      // sub-step 1
-      load_frags(nxt, fa, fa.k0, f0);
-      if (active) mma_16(f1, acc);
-      CCE_INTERLEAVE(0x100, 8)
-    }
-    CCE_WAIT_VMCNT(0);
-    __syncthreads();
+    DmaOperand<AMODE, KTAIL> da;
+    DmaOperand<BMODE, KTAIL> db;
+    da.init(A, K, lane, w);
+    db.init(B, K, lane, w);
+    gemm_loop<SKIP>(da, db, fa, nk, kflags, kflag_stride, ring, lds_addr(ring), acc);
   } else {
     for (int kt = 0; kt < nk; ++kt) {
       const bool active = !SKIP || kflags[(size_t)((kt * BK) / TILE) * kflag_stride] != 0;
       __syncthreads();
-      slow_slice(A, lda, a_rows, K, kt * BK, ring, tid);
-      slow_slice(B, ldb, b_rows, K, kt * BK, ring + HALF_BYTES, tid);
+      slow_slice<AMODE>(A, K, kt * BK, ring, tid);
+      slow_slice<BMODE>(B, K, kt * BK, ring + HALF_BYTES, tid);
       __syncthreads();
       Frags f;
-      load_frags(ring, fa, fa.k0, f);
+      load_frags(ring, fa, 0, f);
       if (active) mma_16(f, acc);
-      load_frags(ring, fa, fa.k1, f);
+      load_frags(ring, fa, 1, f);
       if (active) mma_16(f, acc);
     }
     __syncthreads();

@@ -79,8 +79,8 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
   for (int t = t0 + split * T; t < t_end; ++t) {
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    gemm_tile<VEC, false, KTAIL>(W + (size_t)v0 * D, D, min(TILE, V - v0), Hb, D, hrows, D,
-                                 nullptr, 0, sm, acc);
+    gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D, D, min(TILE, V - v0), D},
+                                 OpRef{Hb, D, hrows, D}, D, nullptr, 0, sm, acc);
     fwd_tile_update<TAIL>(acc, v0 + wi * 128, V, half, m_run, s_run);
   }
 

@@ -60,12 +60,7 @@ struct BwdArgs {
   float filter_eps, block_eps;
   float* dh;
   float* dW;
-  // bf16 workspace matrices in the blocked layout (256-row tiles, each a run
-  // of K/32 blocks of 256 x 32 elements):
-  u16* HT;     // [Dpad, Mpad]
-  u16* WT;     // [Dpad, Vc]
-  u16* G;      // [Mpad, Vc]
-  u16* GT;     // [Vc, Mpad]
+  u16* G;      // [Mpad, Vc] bf16, blocked (256 x 32 blocks)
   int* flags;  // [nMt, Vc / kTile]
   unsigned* status;
 };
