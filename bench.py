@@ -250,10 +250,11 @@ def main():
     flops = 8.0 * wl.M * wl.V * wl.D
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens_s = wl.M / (ms_step * 1e-3)
-    # dominant single kernel timed live: the forward GEMM + online-LSE kernel
-    # (cce_forward = k_fwd + a merge kernel of a few microseconds)
+    # the longest single launch, timed live: the forward GEMM + online-LSE kernel
+    # (cce_forward = k_fwd + target-logit and merge kernels of a few microseconds)
     fwd_flops = 2.0 * wl.M * wl.V * wl.D
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    bwd_tflops = 3.0 * fwd_flops / (bwd_ms * 1e-3) / 1e12
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
         try:
@@ -290,6 +291,12 @@ def main():
                      "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic},
+        # the backward's kernels (per vocab chunk: recompute, then dh + dW) timed
+        # together live around cce_backward: 3 contractions of 2*M*V*D FLOPs
+        "roofline_backward": {"kernels": "k_recompute + k_grads (cce_backward)",
+                              "bound": "mfma", "achieved": round(bwd_tflops, 2),
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
     }
     del dh, dW
     torch.cuda.empty_cache()

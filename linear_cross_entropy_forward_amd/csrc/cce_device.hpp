@@ -448,15 +448,17 @@ __device__ __forceinline__ void read_frag(const unsigned char* stage, const Frag
 // One K step of the pipelined loop (slice kt in stage `cur`; `nxt` holds slice
 // kt+1; `far` receives slice kt+3), in a fixed instruction order:
 //   sub-step 0: 16 MFMAs (A tile i = q/4, B tile j = q%4) on fragments read
-//     earlier; after MFMA q comes, for even q, direct-to-LDS load q/2 of
-//     slice kt+3 into `far` (A, then B; `far` was last read in iteration
-//     kt-1, before the barrier that ended it) and, for odd q, the LDS read of
-//     one of sub-step 1's fragments
-//   wait until this wave's loads of slice kt+1 have landed, then barrier
-//   sub-step 1: 16 MFMAs; after each of the first 8, the read of one of slice
-//     kt+1's first fragments.
-// sched_barrier pins the order: one memory instruction between MFMAs keeps
-// the in-order issue from stalling the MFMA pipe behind a burst of them.
+//     earlier; after MFMA q: for even q the LDS read of one of sub-step 1's
+//     fragments, for q = 3, 7, 11, 15 one direct-to-LDS load of slice kt+3's
+//     A half into `far` (last read in iteration kt-1, before its mid barrier)
+//   wait until this wave's loads of slice kt+1 have landed (in flight may be
+//     slice kt+2's 8 loads and the 4 just issued), then barrier
+//   sub-step 1: 16 MFMAs; after even q the read of one of slice kt+1's first
+//     fragments, after q = 3, 7, 11, 15 one load of slice kt+3's B half.
+// The loads are spread one per 4 MFMAs: the CU's load path moves 64 bytes a
+// clock, and the 4 waves run in step, so bunched loads stall every wave's
+// issue (and crowd the LDS reads they share the LDS with).  sched_barrier
+// pins the order.
 template <int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
 __device__ __forceinline__ void gemm_step(const DmaOperand<AMODE, KTAIL>& da,
                                           const DmaOperand<BMODE, KTAIL>& db,
@@ -465,26 +467,23 @@ __device__ __forceinline__ void gemm_step(const DmaOperand<AMODE, KTAIL>& da,
                                           unsigned far, Frags& f0, Frags& f1,
                                           floatx16 (&acc)[4][4]) {
   const typename DmaOperand<AMODE, KTAIL>::Slice sa = da.slice(kn);
-  const typename DmaOperand<BMODE, KTAIL>::Slice sb = db.slice(kn);
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int i = q >> 2, j = q & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.a[i], f0.b[j], acc[i][j], 0, 0, 0);
-    if ((q & 1) == 0) {
-      if (q < 8) da.issue(sa, far, q >> 1);
-      else db.issue(sb, far + HALF_BYTES, (q >> 1) - 4);
-    } else {
-      read_frag(cur, fa, 1, q >> 1, f1);
-    }
+    if ((q & 1) == 0) read_frag(cur, fa, 1, q >> 1, f1);
+    else if ((q & 3) == 3) da.issue(sa, far, q >> 2);
     __builtin_amdgcn_sched_barrier(0);
   }
-  CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slices kt+2, kt+3 may be in flight)
+  CCE_WAIT_VMCNT(12);  // slice kt+1 landed (slice kt+2 and half of kt+3 may be in flight)
   ring_barrier();
+  const typename DmaOperand<BMODE, KTAIL>::Slice sb = db.slice(kn);
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int i = q >> 2, j = q & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i], f1.b[j], acc[i][j], 0, 0, 0);
-    if (q < 8) read_frag(nxt, fa, 0, q, f0);
+    if ((q & 1) == 0) read_frag(nxt, fa, 0, q >> 1, f0);
+    else if ((q & 3) == 3) db.issue(sb, far + HALF_BYTES, q >> 2);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -494,8 +493,9 @@ __device__ __forceinline__ void gemm_step(const DmaOperand<AMODE, KTAIL>& da,
 // (constant LDS offsets).  The order between the direct-to-LDS loads and the
 // reads of their data is kept by the explicit vmcnt waits and barriers only.
 // SKIP: a slice whose 256-wide K block is flagged inactive streams through
-// the ring without its MFMAs.  This variant branches around each sub-step's
-// 16 MFMAs as a whole (no interleaving, no unrolling): control flow between
+// the ring without its MFMAs.  A tile with every block active takes the
+// regular loop; otherwise a variant that branches around each sub-step's 16
+// MFMAs as a whole (no interleaving, no unrolling): control flow between
 // interleaved MFMAs leaves the register allocator unable to keep the
 // accumulators in place.
 template <bool SKIP, int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
@@ -505,6 +505,16 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
                                           const int* __restrict__ kflags, int kflag_stride,
                                           const unsigned char* ring, unsigned ring_lds,
                                           floatx16 (&acc)[4][4]) {
+  bool all_active = true;
+  if (SKIP) {
+    // one pass over the tile's K-block flags (lanes stride over the blocks),
+    // before any direct-to-LDS load is in flight
+    const int nkb = (nk * BK + TILE - 1) / TILE;
+    bool lane_ok = true;
+    for (int kb = (int)(threadIdx.x & 63); kb < nkb; kb += 64)
+      lane_ok &= kflags[(size_t)kb * kflag_stride] != 0;
+    all_active = __ballot(!lane_ok) == 0ull;
+  }
   const int klast = (nk - 1) * BK;
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) {
@@ -516,7 +526,7 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
   ring_barrier();
   Frags f0, f1;
   load_frags(ring, fa, 0, f0);
-  if (SKIP) {
+  if (SKIP && !all_active) {
     for (int kt = 0; kt < nk; ++kt) {
       const unsigned char* cur = ring + (kt & 3) * STAGE_BYTES;
       const unsigned char* nxt = ring + ((kt + 1) & 3) * STAGE_BYTES;
