@@ -71,30 +71,22 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   return L;
 }
 
-// gfx950 check of the current device and its compute-unit count, cached per
-// device id.
-cce_status device_ok(int* ncu = nullptr) {
+// gfx950 check of the current device, cached per device id.
+cce_status device_ok() {
   static std::mutex mu;
   static int cache[64];  // 0 unknown, 1 ok, 2 not ok
-  static int cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CCE_EDEVICE;
   if (dev < 64) {
     std::lock_guard<std::mutex> g(mu);
-    if (cache[dev] == 1) {
-      if (ncu) *ncu = cus[dev];
-      return CCE_OK;
-    }
-    if (cache[dev] == 2) return CCE_EDEVICE;
+    if (cache[dev] != 0) return cache[dev] == 1 ? CCE_OK : CCE_EDEVICE;
   }
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, dev) != hipSuccess) return CCE_EDEVICE;
   const bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
-  if (ncu) *ncu = p.multiProcessorCount;
   if (dev < 64) {
     std::lock_guard<std::mutex> g(mu);
     cache[dev] = ok ? 1 : 2;
-    cus[dev] = p.multiProcessorCount;
   }
   return ok ? CCE_OK : CCE_EDEVICE;
 }
@@ -199,12 +191,10 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
   const Layout L = layout(M, V, D);
   if (ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return CCE_EWORKSPACE;
-  int ncu = 0;
-  const cce_status ds = device_ok(&ncu);
+  const cce_status ds = device_ok();
   if (ds != CCE_OK) return ds;
   char* base = static_cast<char*>(ws);
   cce::BwdArgs a{};
-  a.ncu8 = ncu >= 8 ? ncu / 8 * 8 : 8;
   a.H = static_cast<const cce::u16*>(h);
   a.W = static_cast<const cce::u16*>(W);
   a.y = y;

@@ -213,7 +213,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     }
     // 2. dh (+)= G W[chunk] and dW[chunk] = G^T h in one launch
     //   dh: A = G (row tiles = token tiles, K = nvt*256), B = W[chunk]^T (row tiles = D tiles)
-    //   dW: A = G^T (row tiles = chunk vocab tiles, K = Mpad), B = h^T
+    //   dW: A = G^T (row tiles = chunk vocab tiles, K = Mpad), B = h^T, both read in place
     {
       const bool skip = a.block_eps > 0.f;
       const int fstride = a.Vc / kTile;

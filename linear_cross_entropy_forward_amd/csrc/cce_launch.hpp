@@ -11,7 +11,7 @@ typedef unsigned short u16;
 // Tile size shared by every kernel (rows of each GEMM operand per workgroup).
 constexpr int kTile = 256;
 // Vocabulary entries per backward chunk: the chunk's bf16 gradient tile
-// G[Mpad, kVocabChunk] (and its transpose) is the V-independent workspace.
+// G[Mpad, kVocabChunk] is the V-independent workspace.
 constexpr int kVocabChunk = 16384;
 // Doubles per pair in the epilogue's pair table.
 constexpr int kPairStride = 16;
@@ -55,7 +55,6 @@ struct BwdArgs {
   const float* coef;
   int M, V, D;
   int nMt, Mpad, Dpad, Vc;
-  int ncu8;      // compute units rounded down to a multiple of 8 (persistent grids)
   bool vec;
   float filter_eps, block_eps;
   float* dh;
