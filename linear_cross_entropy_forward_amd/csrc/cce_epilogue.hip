@@ -49,18 +49,36 @@ __global__ __launch_bounds__(256) void k_epi_pairs(const float* __restrict__ log
   double sc = 0, sr = 0, sp = 0;
   int nc = 0, nr = 0, np = 0;
   unsigned err = 0u;
-  for (int i = tid; i < M; i += 256) {
-    const int s = seg[i];
-    const int kind = s & 3, pr = s >> 2;
-    if (b == 0) {
-      if (pr < 0 || pr >= B) err |= 2u;                       // CCE_DERR_PAIR
-      if (kind != 0 && y[i] < 0) err |= 1u;                    // CCE_DERR_TARGET
+  // Thread tid visits rows tid, tid + 256, tid + 512, ... in that order; the
+  // loads of 8 of them are issued together so the scan is not one memory
+  // latency per row.
+  constexpr int U = 8;
+  for (int base = 0; base < M; base += 256 * U) {
+    int sv[U], yv[U];
+    float lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * 256 + tid;
+      const bool in = i < M;
+      sv[u] = in ? seg[i] : -4;  // pair -1: matches no pair, checked by nobody
+      lv[u] = in ? logp[i] : 0.f;
+      yv[u] = (in && b == 0) ? y[i] : 0;
     }
-    if (pr != b) continue;
-    const double lp = (double)logp[i];
-    if (kind == 2) { sc += lp; ++nc; }
-    else if (kind == 3) { sr += lp; ++nr; }
-    else if (kind == 1) { sp += lp; ++np; }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * 256 + tid >= M) continue;
+      const int s = sv[u];
+      const int kind = s & 3, pr = s >> 2;
+      if (b == 0) {
+        if (pr < 0 || pr >= B) err |= 2u;                       // CCE_DERR_PAIR
+        if (kind != 0 && yv[u] < 0) err |= 1u;                  // CCE_DERR_TARGET
+      }
+      if (pr != b) continue;
+      const double lp = (double)lv[u];
+      if (kind == 2) { sc += lp; ++nc; }
+      else if (kind == 3) { sr += lp; ++nr; }
+      else if (kind == 1) { sp += lp; ++np; }
+    }
   }
   if (err) atomicOr(status, err);
   sh[0][tid] = sc; sh[1][tid] = sr; sh[2][tid] = sp;

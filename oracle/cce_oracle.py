@@ -27,7 +27,11 @@ reason in the design notes of the repository):
     log-odds;
   * the gradient filter compares the softmax value itself with eps and never
     drops the target entry;
-  * a row with target -1 is ignored: its log-prob is 0 and its coefficient 0.
+  * a row with target -1 is ignored: its log-prob is 0 and its coefficient 0;
+  * the final-logit softcap is cap * tanh(z / cap) evaluated exactly (the pages'
+    head divides by a bf16-rounded cap inside its framework's op; here the cap
+    is a plain float argument), applied before both the log-sum-exp and the
+    target gather, with sech^2(z / cap) in the backward; cap = 0 means off.
 
 Every function here has a pin in the test-suite (closed forms, library special
 cases, finite differences, brute force, invariants); none is "parity unpinned"
@@ -61,15 +65,32 @@ def logits(H: np.ndarray, W: np.ndarray) -> np.ndarray:
     return np.asarray(H, np.float64) @ np.asarray(W, np.float64).T
 
 
+def capped(Z: np.ndarray, softcap: float) -> np.ndarray:
+    """Final-logit softcap ([P1] §5.1, the e4b head with cap 30; [P2] lever 1
+    "Implementation spec"): cap * tanh(z / cap); softcap = 0 leaves Z as is."""
+    if softcap == 0.0:
+        return Z
+    return softcap * np.tanh(Z / softcap)
+
+
+def dcapped(Z: np.ndarray, softcap: float) -> np.ndarray:
+    """d capped / d z = sech^2(z / cap) = 1 - tanh^2(z / cap) (1 when off)."""
+    if softcap == 0.0:
+        return np.ones_like(Z)
+    t = np.tanh(Z / softcap)
+    return 1.0 - t * t
+
+
 def logsumexp_rows(Z: np.ndarray) -> np.ndarray:
     """log sum_v exp(Z[i, v]) with the row max factored out."""
     m = Z.max(axis=1)
     return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
 
 
-def forward(H: np.ndarray, W: np.ndarray, y: np.ndarray):
+def forward(H: np.ndarray, W: np.ndarray, y: np.ndarray, softcap: float = 0.0):
     """Returns (logp[M], lse[M]) in fp64.  Rows with y = -1 get logp = 0 (their
-    lse is still computed)."""
+    lse is still computed).  With softcap > 0 every logit is capped first
+    (both the log-sum-exp and the target logit see the capped value)."""
     H = np.asarray(H, np.float64)
     W = np.asarray(W, np.float64)
     y = np.asarray(y, np.int64)
@@ -79,7 +100,7 @@ def forward(H: np.ndarray, W: np.ndarray, y: np.ndarray):
     step = _row_chunk(V)
     for i0 in range(0, M, step):
         i1 = min(M, i0 + step)
-        Z = logits(H[i0:i1], W)
+        Z = capped(logits(H[i0:i1], W), softcap)
         lse[i0:i1] = logsumexp_rows(Z)
         yy = y[i0:i1]
         ok = yy >= 0
@@ -88,11 +109,12 @@ def forward(H: np.ndarray, W: np.ndarray, y: np.ndarray):
     return logp, lse
 
 
-def forward_rows(H: np.ndarray, W: np.ndarray, y: np.ndarray, rows: np.ndarray):
+def forward_rows(H: np.ndarray, W: np.ndarray, y: np.ndarray, rows: np.ndarray,
+                 softcap: float = 0.0):
     """The forward for a subset of rows only (used for sampled checks at large
     sizes)."""
     rows = np.asarray(rows, np.int64)
-    lp, ls = forward(np.asarray(H)[rows], W, np.asarray(y)[rows])
+    lp, ls = forward(np.asarray(H)[rows], W, np.asarray(y)[rows], softcap)
     return lp, ls
 
 
@@ -249,20 +271,25 @@ def loss_from_logp(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, 
 # G = coef (softmax - onehot); dh = G W and dW = G^T H.
 # Filter mode ([P1] §5.1 skips; [P3] "The coeff filter"): softmax entries
 # below eps are dropped, never the target's.
+# Softcap ([P1] §5.1; [P2] lever 1 "Implementation spec"): the softmax is that
+# of the capped logits, and the chain rule through the cap multiplies each
+# entry by sech^2(z / cap).
 # ----------------------------------------------------------------------------
 def grad_logits(Z: np.ndarray, lse: np.ndarray, y: np.ndarray, coef: np.ndarray,
-                filter_eps: float = 0.0) -> np.ndarray:
-    P = np.exp(Z - lse[:, None])
+                filter_eps: float = 0.0, softcap: float = 0.0) -> np.ndarray:
+    """G = coef * (softmax(capped Z) - onehot) * d capped / d z, from the raw
+    logits Z."""
+    P = np.exp(capped(Z, softcap) - lse[:, None])
     onehot = np.zeros_like(P)
     rows = np.nonzero(y >= 0)[0]
     onehot[rows, y[rows]] = 1.0
     if filter_eps > 0.0:
         P = np.where((P < filter_eps) & (onehot == 0.0), 0.0, P)
-    return coef[:, None] * (P - onehot)
+    return coef[:, None] * (P - onehot) * dcapped(Z, softcap)
 
 
 def backward(H: np.ndarray, W: np.ndarray, y: np.ndarray, lse: np.ndarray, coef: np.ndarray,
-             filter_eps: float = 0.0):
+             filter_eps: float = 0.0, softcap: float = 0.0):
     """Returns (dh[M,D], dW[V,D]) in fp64, given the forward's lse and the
     epilogue's coef."""
     H = np.asarray(H, np.float64)
@@ -276,24 +303,25 @@ def backward(H: np.ndarray, W: np.ndarray, y: np.ndarray, lse: np.ndarray, coef:
     step = _row_chunk(V)
     for i0 in range(0, M, step):
         i1 = min(M, i0 + step)
-        G = grad_logits(logits(H[i0:i1], W), lse[i0:i1], y[i0:i1], coef[i0:i1], filter_eps)
+        G = grad_logits(logits(H[i0:i1], W), lse[i0:i1], y[i0:i1], coef[i0:i1], filter_eps,
+                        softcap)
         dh[i0:i1] = G @ W
         dW += G.T @ H[i0:i1]
     return dh, dW
 
 
-def backward_dh_rows(H, W, y, lse, coef, rows, filter_eps: float = 0.0):
+def backward_dh_rows(H, W, y, lse, coef, rows, filter_eps: float = 0.0, softcap: float = 0.0):
     """dh for a subset of rows (each row of dh depends only on its own row)."""
     rows = np.asarray(rows, np.int64)
     H = np.asarray(H, np.float64)
     W = np.asarray(W, np.float64)
     Z = logits(H[rows], W)
     G = grad_logits(Z, np.asarray(lse, np.float64)[rows], np.asarray(y, np.int64)[rows],
-                    np.asarray(coef, np.float64)[rows], filter_eps)
+                    np.asarray(coef, np.float64)[rows], filter_eps, softcap)
     return G @ W
 
 
-def backward_dW_rows(H, W, y, lse, coef, vrows, filter_eps: float = 0.0):
+def backward_dW_rows(H, W, y, lse, coef, vrows, filter_eps: float = 0.0, softcap: float = 0.0):
     """dW for a subset of vocab rows: dW[v] = sum_i G[i, v] h_i, which needs the
     logits of every row against those vocab rows only (lse for all rows is
     an input)."""
@@ -304,18 +332,19 @@ def backward_dW_rows(H, W, y, lse, coef, vrows, filter_eps: float = 0.0):
     lse = np.asarray(lse, np.float64)
     coef = np.asarray(coef, np.float64)
     Z = H @ W[vrows].T                                   # [M, |vrows|]
-    P = np.exp(Z - lse[:, None])
+    P = np.exp(capped(Z, softcap) - lse[:, None])
     onehot = (y[:, None] == vrows[None, :]).astype(np.float64)
     if filter_eps > 0.0:
         P = np.where((P < filter_eps) & (onehot == 0.0), 0.0, P)
-    G = coef[:, None] * (P - onehot)
+    G = coef[:, None] * (P - onehot) * dcapped(Z, softcap)
     return G.T @ H
 
 
-def step(H, W, y, seg, n_pairs, lam, scope, filter_eps: float = 0.0) -> Dict:
+def step(H, W, y, seg, n_pairs, lam, scope, filter_eps: float = 0.0,
+         softcap: float = 0.0) -> Dict:
     """One whole pass: forward, epilogue, backward."""
-    logp, lse = forward(H, W, y)
+    logp, lse = forward(H, W, y, softcap)
     ep = epilogue(logp, seg, n_pairs, lam, scope)
-    dh, dW = backward(H, W, y, lse, ep["coef"], filter_eps)
+    dh, dW = backward(H, W, y, lse, ep["coef"], filter_eps, softcap)
     ep.update(logp=logp, lse=lse, dh=dh, dW=dW)
     return ep

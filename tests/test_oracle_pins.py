@@ -515,3 +515,100 @@ def test_zipf_histogram():
         expect = p[k] * 200000
         assert abs(counts[k] - expect) < 4.0 * math.sqrt(expect)     # 4 sigma
     assert ids.min() >= 0 and ids.max() < V
+
+
+# ----------------------------------------------------------------------------
+# P10: final-logit softcap ([P1] §5.1, the e4b head with cap 30; [P2] lever 1
+# "Implementation spec": logit = cap * tanh(raw / cap), folded into both the
+# log-sum-exp and the backward, d logit / d raw = sech^2(raw / cap))
+# ----------------------------------------------------------------------------
+def test_p10_softcap_binds_closed_form():
+    """One raw logit far above the cap: the capped logit is the cap itself, so
+    logp = cap - log(e^cap + (V - 1)) for that target and -log(e^cap + V - 1)
+    for any other (an uncapped head would give about 0 and about -1e4)."""
+    V, cap = 5, 30.0
+    H = np.array([[1.0], [1.0]])
+    W = np.array([[1.0e4], [0.0], [0.0], [0.0], [0.0]])
+    y = np.array([0, 3])
+    logp, lse = O.forward(H, W, y, softcap=cap)
+    den = math.log(math.exp(cap) + (V - 1))
+    assert logp[0] == pytest.approx(cap - den, rel=1e-14, abs=1e-15)
+    assert logp[1] == pytest.approx(-den, rel=1e-14)
+    assert lse[0] == pytest.approx(den, rel=1e-14)
+
+
+def test_p10_softcap_large_cap_is_uncapped():
+    wl = _case()
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    lp0, ls0 = O.forward(H, W, y)
+    lp1, ls1 = O.forward(H, W, y, softcap=1.0e7)
+    np.testing.assert_allclose(lp1, lp0, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(ls1, ls0, rtol=1e-9)
+    coef = O.epilogue(lp0, seg, 2, wl.lam, O.SCOPE_FULL)["coef"]
+    dh0, dW0 = O.backward(H, W, y, ls0, coef)
+    dh1, dW1 = O.backward(H, W, y, ls1, coef, softcap=1.0e7)
+    np.testing.assert_allclose(dh1, dh0, rtol=1e-8, atol=1e-14)
+    np.testing.assert_allclose(dW1, dW0, rtol=1e-8, atol=1e-14)
+
+
+def test_p10_softcap_torch_autograd():
+    """Forward and the analytic backward with a cap that binds (logit scale
+    several times the cap) equal torch fp64 autograd through cap * tanh."""
+    torch = pytest.importorskip("torch")
+    spans = [(3, 6, 5, 2), (1, 4, 4)]
+    wl = WL.make_custom(spans, D=12, V=23, seed=17, hidden_scale=3.0, w_std=1.0, lam=0.5)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    cap = 2.5
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    Z = cap * torch.tanh((Ht @ Wt.T) / cap)
+    lsm = torch.log_softmax(Z, dim=1)
+    lp_t = lsm[torch.arange(len(y)), torch.tensor(np.maximum(y, 0))] * torch.tensor(y >= 0)
+    logp, lse = O.forward(H, W, y, softcap=cap)
+    np.testing.assert_allclose(logp, lp_t.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(Z, 1).detach().numpy(), rtol=1e-13)
+    ep = O.epilogue(logp, seg, 2, wl.lam, O.SCOPE_FULL)
+    # the loss as a function of lp_t, through the oracle's coef (dL/dlogp = -coef)
+    (-(torch.tensor(ep["coef"]) * lp_t).sum()).backward()
+    dh, dW = O.backward(H, W, y, lse, ep["coef"], softcap=cap)
+    np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-14)
+
+
+def test_p10_softcap_finite_differences():
+    spans = [(2, 3, 2, 1), (1, 2, 3)]
+    wl = WL.make_custom(spans, D=5, V=9, seed=23, hidden_scale=2.5, w_std=1.2, lam=0.3)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    cap = 1.5
+
+    def L(Hx, Wx):
+        lp, _ = O.forward(Hx, Wx, y, softcap=cap)
+        return O.epilogue(lp, seg, 2, wl.lam, O.SCOPE_FULL)["loss"]
+
+    logp, lse = O.forward(H, W, y, softcap=cap)
+    ep = O.epilogue(logp, seg, 2, wl.lam, O.SCOPE_FULL)
+    dh, dW = O.backward(H, W, y, lse, ep["coef"], softcap=cap)
+    eps = 1e-6
+    fdH = np.zeros_like(H)
+    for i in range(H.shape[0]):
+        for d in range(H.shape[1]):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, d] += eps
+            Hm[i, d] -= eps
+            fdH[i, d] = (L(Hp, W) - L(Hm, W)) / (2 * eps)
+    fdW = np.zeros_like(W)
+    for v in range(W.shape[0]):
+        for d in range(W.shape[1]):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[v, d] += eps
+            Wm[v, d] -= eps
+            fdW[v, d] = (L(H, Wp) - L(H, Wm)) / (2 * eps)
+    assert np.linalg.norm(dh - fdH) / np.linalg.norm(fdH) < 1e-6
+    assert np.linalg.norm(dW - fdW) / np.linalg.norm(fdW) < 1e-6
+    # the cap matters here: the same gradient with the sech^2 factor dropped
+    # (softmax of the capped logits, no chain rule through the cap) is far off
+    Zc = cap * np.tanh((H @ W.T) / cap)
+    onehot = np.zeros_like(Zc)
+    onehot[np.nonzero(y >= 0)[0], y[y >= 0]] = 1.0
+    dh_nosech = (ep["coef"][:, None] * (np.exp(Zc - lse[:, None]) - onehot)) @ W
+    assert np.linalg.norm(dh_nosech - fdH) / np.linalg.norm(fdH) > 1e-2
