@@ -33,6 +33,8 @@ def parse():
                     help="coefficient filter eps (default: the workload's own setting)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="final-logit softcap c (logits c*tanh(z/c)); 0 = off (the metric's config)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
     ap.add_argument("--v-sweep", action="store_true",
                     help="time one step and record workspace / peak device memory at "
@@ -212,13 +214,13 @@ def main():
     def one_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        head.forward(h, W, y, logp, lse, stream=stream)
+        head.forward(h, W, y, logp, lse, stream=stream, softcap=args.softcap)
         if ev is not None:
             ev[1].record(stream)
         head.epilogue(logp, y, seg, wl.n_pairs, wl.lam, wl.scope, out5, pst, coef, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        head.backward(h, W, y, lse, coef, feps, feps, dh, dW, stream=stream)
+        head.backward(h, W, y, lse, coef, feps, feps, dh, dW, stream=stream, softcap=args.softcap)
         if ev is not None:
             ev[3].record(stream)
 
@@ -280,7 +282,7 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden, N(0,0.02^2) head, Zipf(1.1) targets)",
         "config": {"workload": wl.name, "M": wl.M, "V": wl.V, "D": wl.D, "n_pairs": wl.n_pairs,
                    "lambda": wl.lam, "scope": "full" if wl.scope == 0 else "response",
-                   "filter_eps": feps, "parallelism": "none (1 GPU)"},
+                   "filter_eps": feps, "softcap": args.softcap, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "phase_ms": {"forward": round(fwd_ms, 4), "epilogue": round(epi_ms, 4),

@@ -85,6 +85,11 @@ size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D);
  *   h        [M, D] bf16 row-major (16-byte aligned rows are the fast path)
  *   W        [V, D] bf16 row-major
  *   y        [M] int32 target ids in [0, V), or -1 for an ignored row
+ *   softcap  0 (off) or the final-logit cap c > 0: every logit becomes
+ *            z = c tanh(h_i . W_v / c) before the log-sum-exp and the target
+ *            gather ("Training — design …" §5.1, the e4b head with c = 30;
+ *            "ORPO training — design", lever 1 spec).  Finite and >= 0, else
+ *            CCE_EINVAL.
  *   logp     [M] fp32 out: z_{i,y_i} - lse_i, and 0 for rows with y_i = -1
  *   lse      [M] fp32 out: logsumexp_v z_{i,v} (written for every row)
  *   dev_status  uint32 (device) OR-ed with CCE_DERR_TARGET / _NONFINITE
@@ -92,7 +97,7 @@ size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D);
  *                 bytes, 256-byte aligned; contents on entry are ignored.
  */
 cce_status cce_forward(const void* h, const void* W, const int32_t* y,
-                       int64_t M, int64_t V, int64_t D,
+                       int64_t M, int64_t V, int64_t D, float softcap,
                        float* logp, float* lse, uint32_t* dev_status,
                        void* ws, size_t ws_bytes, void* stream);
 
@@ -125,10 +130,13 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
 
 /*
  * Backward of the head given the per-row coefficient coef_i = -dL/dlogp_i:
- *   G_{i,v} = coef_i (softmax_{i,v} - [v = y_i]),  dh = G W,  dW = G^T h.
+ *   G_{i,v} = coef_i (softmax_{i,v} - [v = y_i]) s_{i,v},  dh = G W,  dW = G^T h,
+ *   with s = 1 - tanh^2(h_i . W_v / c) under a softcap c, else 1.
  *   "Training — design …" §5.1 (analytic backward from the saved LSE;
- *   backward skips); "ORPO training — design", lever 1 spec (backward).
- *   h, W, y  as for cce_forward;  lse [M], coef [M] fp32.
+ *   backward skips; the sech^2 factor of the capped head); "ORPO training —
+ *   design", lever 1 spec (backward).
+ *   h, W, y, softcap  as for cce_forward (the same softcap as the forward that
+ *            produced lse);  lse [M], coef [M] fp32.
  *   filter_eps  >= 0; softmax entries below it are dropped (never the target's).
  *   block_eps   >= 0; a 256x256 (row, vocab) tile whose largest softmax entry
  *               is below it and that holds no row's target is skipped.
@@ -139,7 +147,7 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
  */
 cce_status cce_backward(const void* h, const void* W, const int32_t* y,
                         const float* lse, const float* coef,
-                        int64_t M, int64_t V, int64_t D,
+                        int64_t M, int64_t V, int64_t D, float softcap,
                         float filter_eps, float block_eps,
                         float* dh, float* dW, uint32_t* dev_status,
                         void* ws, size_t ws_bytes, void* stream);

@@ -27,11 +27,12 @@ SIGNATURES = {
     "cce_abi_version": (ctypes.c_int, []),
     "cce_status_string": (ctypes.c_char_p, [_c_i]),
     "cce_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
-    "cce_forward": (_c_i, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_forward": (_c_i, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz,
+                           _c_p]),
     "orpo_epilogue": (_c_i, [_c_p, _c_p, _c_p, _c_i64, ctypes.c_int32, _c_f, _c_i, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_sz, _c_p]),
-    "cce_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_f, _c_p,
-                            _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_f, _c_f,
+                            _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
 }
 
 _lib = None
@@ -128,14 +129,14 @@ class Head:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     # -- forward --------------------------------------------------------------
-    def forward(self, h, W, y, logp=None, lse=None, stream=None):
+    def forward(self, h, W, y, logp=None, lse=None, stream=None, softcap: float = 0.0):
         M, V, D = self.M, self.V, self.D
         if logp is None:
             logp = torch.empty(M, dtype=torch.float32, device=self.device)
         if lse is None:
             lse = torch.empty(M, dtype=torch.float32, device=self.device)
         st = load().cce_forward(_bf16(h, "h", (M, D)), _bf16(W, "W", (V, D)),
-                                _dev(y, "y", torch.int32, (M,)), M, V, D,
+                                _dev(y, "y", torch.int32, (M,)), M, V, D, float(softcap),
                                 _dev(logp, "logp", torch.float32, (M,)),
                                 _dev(lse, "lse", torch.float32, (M,)),
                                 self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
@@ -164,7 +165,7 @@ class Head:
 
     # -- backward -------------------------------------------------------------
     def backward(self, h, W, y, lse, coef, filter_eps: float = 0.0, block_eps: float = 0.0,
-                 dh=None, dW=None, stream=None):
+                 dh=None, dW=None, stream=None, softcap: float = 0.0):
         M, V, D = self.M, self.V, self.D
         if dh is None:
             dh = torch.empty((M, D), dtype=torch.float32, device=self.device)
@@ -174,7 +175,7 @@ class Head:
                                  _dev(y, "y", torch.int32, (M,)),
                                  _dev(lse, "lse", torch.float32, (M,)),
                                  _dev(coef, "coef", torch.float32, (M,)), M, V, D,
-                                 float(filter_eps), float(block_eps),
+                                 float(softcap), float(filter_eps), float(block_eps),
                                  _dev(dh, "dh", torch.float32, (M, D)),
                                  _dev(dW, "dW", torch.float32, (V, D)),
                                  self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
@@ -196,9 +197,10 @@ def to_device_bits(bits, device) -> torch.Tensor:
     return t.to(device).view(torch.bfloat16)
 
 
-def step(head: Head, h, W, y, seg, n_pairs, lam, scope, filter_eps=0.0, block_eps=0.0, stream=None):
+def step(head: Head, h, W, y, seg, n_pairs, lam, scope, filter_eps=0.0, block_eps=0.0, stream=None,
+         softcap=0.0):
     """One whole pass: forward, epilogue, backward (all enqueued on one stream)."""
-    logp, lse = head.forward(h, W, y, stream=stream)
+    logp, lse = head.forward(h, W, y, stream=stream, softcap=softcap)
     out5, pstats, coef = head.epilogue(logp, y, seg, n_pairs, lam, scope, stream=stream)
-    dh, dW = head.backward(h, W, y, lse, coef, filter_eps, block_eps, stream=stream)
+    dh, dW = head.backward(h, W, y, lse, coef, filter_eps, block_eps, stream=stream, softcap=softcap)
     return dict(logp=logp, lse=lse, out5=out5, pair_stats=pstats, coef=coef, dh=dh, dW=dW)

@@ -97,7 +97,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int cce_abi_version(void) { return 1; }
+int cce_abi_version(void) { return 2; }
 
 const char* cce_status_string(int status) {
   switch (status) {
@@ -117,9 +117,10 @@ size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D) {
 }
 
 cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M, int64_t V,
-                       int64_t D, float* logp, float* lse, uint32_t* dev_status, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       int64_t D, float softcap, float* logp, float* lse, uint32_t* dev_status,
+                       void* ws, size_t ws_bytes, void* stream) {
   if (!h || !W || !y || !logp || !lse || !dev_status || !ws) return CCE_EINVAL;
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
   const Layout L = layout(M, V, D);
   if (ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0) return CCE_EWORKSPACE;
@@ -139,6 +140,7 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
   if (V / kTile > 0) fwd_split(a.nMt, V / kTile, a.S, a.T);  // over the full vocab tiles
   a.Mpad = (int)L.Mpad;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
+  a.softcap = softcap;
   a.part_m = reinterpret_cast<float*>(base + L.part_m);
   a.part_s = reinterpret_cast<float*>(base + L.part_s);
   a.tgt = reinterpret_cast<float*>(base + L.tgt);
@@ -182,10 +184,11 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
 }
 
 cce_status cce_backward(const void* h, const void* W, const int32_t* y, const float* lse,
-                        const float* coef, int64_t M, int64_t V, int64_t D, float filter_eps,
-                        float block_eps, float* dh, float* dW, uint32_t* dev_status, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const float* coef, int64_t M, int64_t V, int64_t D, float softcap,
+                        float filter_eps, float block_eps, float* dh, float* dW,
+                        uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!h || !W || !y || !lse || !coef || !dh || !dW || !dev_status || !ws) return CCE_EINVAL;
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
   if (!(filter_eps >= 0.f) || !(block_eps >= 0.f) || !isfinite(filter_eps) || !isfinite(block_eps))
     return CCE_EINVAL;
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
@@ -208,6 +211,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.Dpad = (int)L.Dpad;
   a.Vc = (int)L.Vc;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
+  a.softcap = softcap;
   a.filter_eps = filter_eps;
   a.block_eps = block_eps;
   a.dh = dh;

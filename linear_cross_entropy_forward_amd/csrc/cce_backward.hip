@@ -7,8 +7,9 @@
 //   G[i, v] = coef_i (softmax(i, v) - [v = y_i]),  dh = G W,  dW = G^T h.
 //
 // The vocabulary is walked in chunks of kVocabChunk entries.  Per chunk:
-//   1. recompute z = h W[chunk]^T, G = coef (softmax - onehot), optional
-//      filter / tile skip; G written as bf16 (RNE)                 MFMA
+//   1. recompute z = h W[chunk]^T, G = coef (softmax - onehot) (times
+//      sech^2(z / c) under a softcap c), optional filter / tile skip; G
+//      written as bf16 (RNE)                                         MFMA
 //   2. dh (+)= G W[chunk] and dW[chunk] = G^T h, one launch          MFMA
 // All three contractions run on the same GEMM core; the transposed operands
 // of step 2 (W[chunk] and h with K = vocab / tokens, and G^T) are read in
@@ -31,12 +32,17 @@ namespace cce {
 // tile.  One workgroup per tile; workgroup b takes logical tile
 // (b % 8)*(n/8) + b/8 of the grouped raster (n = launch size, a multiple of
 // 8), i.e. each XCD works on a contiguous run of tiles.
-template <bool VEC, bool FILTER, bool KTAIL>
+//
+// CAP (final-logit softcap c): the accumulators keep t = tanh(z / c); the
+// softmax entry is exp(c t - lse) and the chain rule through the cap adds the
+// factor 1 - t^2 (sech^2(z / c)).  The tile-skip test uses the per-token
+// largest t, which gives the largest softmax entry of that token.
+template <bool VEC, bool FILTER, bool KTAIL, bool CAP>
 __global__ __launch_bounds__(NT, 1) void k_recompute(
     const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
     const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
-    int vlen, int nMt, int nvt, float filter_eps, float block_eps, u16* __restrict__ G,
-    int* __restrict__ flags, int nkbV) {
+    int vlen, int nMt, int nvt, float softcap, float filter_eps, float block_eps,
+    u16* __restrict__ G, int* __restrict__ flags, int nkbV) {
   __shared__ Smem sm;
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -64,9 +70,13 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
     const int o = (yy >= 0) ? yy - (v0 + vl0) : -1;
     any_tgt_lane |= (unsigned)o < 128u;
   }
-  // softmax entries into acc; rows beyond the chunk's valid vocab become 0
+  // softmax entries into acc (CAP: tanh(z / c)); rows beyond the chunk's
+  // valid vocab become 0 (CAP: they are masked again at the store)
   const bool vtail = vt * TILE + TILE > vlen;
+  const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;
+  const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
   float pmax = 0.f;
+  float tmax[4] = {-1.f, -1.f, -1.f, -1.f};
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
@@ -74,12 +84,22 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
       const bool vbad = vtail && (vl0 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= vlen);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float p = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nlse[jj]));
-        if (vbad) p = 0.f;
-        acc[ii][jj][r] = p;
-        pmax = fmaxf(pmax, p);
+        if (CAP) {
+          const float t = tanh_scaled(acc[ii][jj][r], k2);
+          acc[ii][jj][r] = t;
+          if (!vbad) tmax[jj] = fmaxf(tmax[jj], t);
+        } else {
+          float p = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nlse[jj]));
+          if (vbad) p = 0.f;
+          acc[ii][jj][r] = p;
+          pmax = fmaxf(pmax, p);
+        }
       }
     }
+  if (CAP) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) pmax = fmaxf(pmax, fast_exp2(fmaf(tmax[jj], c1, nlse[jj])));
+  }
   int* flag = flags + (size_t)mt * (nkbV / 8) + vt;
   if (block_eps > 0.f) {
     // skip the tile if every softmax entry is below block_eps and no token of
@@ -111,10 +131,18 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
         float g[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float p = acc[ii][jj][4 * q + e];
+          float p, sech2 = 1.f;
+          if (CAP) {
+            const float t = acc[ii][jj][4 * q + e];
+            const bool vbad = vtail && (vl0 + ii * 32 + 8 * q + 4 * half + e >= vlen);
+            p = vbad ? 0.f : fast_exp2(fmaf(t, c1, nlse[jj]));
+            sech2 = 1.f - t * t;
+          } else {
+            p = acc[ii][jj][4 * q + e];
+          }
           const bool is_t = wave_has_tgt && (off[jj] == ii * 32 + 8 * q + e);
           if (FILTER && p < filter_eps && !is_t) p = 0.f;
-          g[e] = cf[jj] * (is_t ? p - 1.f : p);
+          g[e] = cf[jj] * (is_t ? p - 1.f : p) * sech2;
         }
         *reinterpret_cast<u32x2*>(gt + (size_t)ii * 8192 + tj * 32 + 8 * q) =
             u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
@@ -196,18 +224,24 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     // 1. recompute + gradient tile
     {
       const int n = pad8(a.nMt * nvt);
-#define CCE_RECOMPUTE(VEC, FILT, KT)                                                               \
-  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y, a.lse,  \
-                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, a.filter_eps, a.block_eps, a.G,       \
-                     a.flags, nkbV)
+#define CCE_RECOMPUTE(VEC, FILT, KT, CAP)                                                          \
+  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y,    \
+                     a.lse, a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, a.softcap, a.filter_eps,       \
+                     a.block_eps, a.G, a.flags, nkbV)
+#define CCE_RECOMPUTE_F(VEC, KT, CAP)                                                              \
+  do {                                                                                             \
+    if (filt) CCE_RECOMPUTE(VEC, true, KT, CAP); else CCE_RECOMPUTE(VEC, false, KT, CAP);          \
+  } while (0)
       const bool kt = a.D % BK != 0;
+      const bool cap = a.softcap > 0.f;
       if (!a.vec) {
-        if (filt) CCE_RECOMPUTE(false, true, false); else CCE_RECOMPUTE(false, false, false);
+        if (cap) CCE_RECOMPUTE_F(false, false, true); else CCE_RECOMPUTE_F(false, false, false);
       } else if (kt) {
-        if (filt) CCE_RECOMPUTE(true, true, true); else CCE_RECOMPUTE(true, false, true);
+        if (cap) CCE_RECOMPUTE_F(true, true, true); else CCE_RECOMPUTE_F(true, true, false);
       } else {
-        if (filt) CCE_RECOMPUTE(true, true, false); else CCE_RECOMPUTE(true, false, false);
+        if (cap) CCE_RECOMPUTE_F(true, false, true); else CCE_RECOMPUTE_F(true, false, false);
       }
+#undef CCE_RECOMPUTE_F
 #undef CCE_RECOMPUTE
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -61,6 +61,15 @@ __device__ __forceinline__ u16 to_bf16(float x) {
   return __builtin_bit_cast(u16, b);
 }
 
+// tanh(z / cap) for the final-logit softcap, as 1 - 2 / (e^{2z/cap} + 1) with
+// k2 = 2 log2(e) / cap: one exp2 and one reciprocal, exact limits +-1 at
+// +-infinity, absolute error about 1e-7 (the cancellation near 0 costs
+// relative, not absolute, accuracy).
+__device__ __forceinline__ float tanh_scaled(float z, float k2) {
+  const float e = fast_exp2(z * k2);
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 // Merge two (max, sum-exp) states of the online softmax.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);

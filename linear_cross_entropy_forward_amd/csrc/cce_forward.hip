@@ -4,7 +4,9 @@
 // "Training — design (ORPO, flash-CCE head, …)" §5.1 and "ORPO training —
 // design", lever 1 "Implementation spec": for each vocab tile take the running
 // max m and sum s of exp(z - m), rescaling s when m grows; the target logit
-// h_i . W_{y_i}; lse = m + log s, logp = tgt - lse.
+// h_i . W_{y_i}; lse = m + log s, logp = tgt - lse.  With the final-logit
+// softcap (same passages; the e4b head) every logit, the target's included,
+// is cap * tanh(z / cap) before any of this.
 //
 // Work split: workgroup (mt, split) owns 256 token rows and a contiguous run of
 // T full vocab tiles of 256.  Each lane keeps (m, s) for the 4 tokens it owns
@@ -53,11 +55,12 @@ __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int
 }
 
 // Workgroup (mt, split) runs vocab tiles [t0 + split*T, min(t0 + (split+1)*T, t1))
-// and writes partial slot slot0 + split.
-template <bool VEC, bool KTAIL, bool TAIL>
+// and writes partial slot slot0 + split.  CAP: every logit is replaced by
+// softcap * tanh(z / softcap) before the online update.
+template <bool VEC, bool KTAIL, bool TAIL, bool CAP>
 __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const u16* __restrict__ W,
                                                int M, int V, int D, int nMt, int S, int T, int t0,
-                                               int t1, int slot0, int nlaunch,
+                                               int t1, int slot0, int nlaunch, float softcap,
                                                float* __restrict__ part_m,
                                                float* __restrict__ part_s, int Mpad) {
   __shared__ Smem sm;
@@ -81,6 +84,15 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
     floatx16 acc[4][4];
     gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D, D, min(TILE, V - v0), D},
                                  OpRef{Hb, D, hrows, D}, D, nullptr, 0, sm, acc);
+    if (CAP) {
+      const float k2 = 2.f * LOG2E / softcap;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[ii][jj][r] = softcap * tanh_scaled(acc[ii][jj][r], k2);
+    }
     fwd_tile_update<TAIL>(acc, v0 + wi * 128, V, half, m_run, s_run);
   }
 
@@ -115,12 +127,14 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
   }
 }
 
-// tgt[i] = h_i . W_{y_i} (fp32 sum of exact bf16 products), one wave per row.
-// Rows whose target is outside [0, V) are skipped (the merge reports them).
+// tgt[i] = h_i . W_{y_i} (fp32 sum of exact bf16 products), one wave per row,
+// then capped like every other logit when softcap > 0.  Rows whose target is
+// outside [0, V) are skipped (the merge reports them).
 __global__ __launch_bounds__(256) void k_target_logit(const u16* __restrict__ H,
                                                       const u16* __restrict__ W,
                                                       const int* __restrict__ y, int M, int V,
-                                                      int D, float* __restrict__ tgt) {
+                                                      int D, float softcap,
+                                                      float* __restrict__ tgt) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
@@ -136,6 +150,7 @@ __global__ __launch_bounds__(256) void k_target_logit(const u16* __restrict__ H,
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (softcap > 0.f) s = softcap * tanh_scaled(s, 2.f * LOG2E / softcap);
   if (lane == 0) tgt[row] = s;
 }
 
@@ -171,12 +186,17 @@ static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int
                              hipStream_t st) {
   const int n = a.nMt * S;
   const int nl = (n + 7) / 8 * 8;
-#define CCE_FWD(VEC, KT)                                                                         \
-  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D, \
-                     a.nMt, S, T, t0, t1, slot0, nl, a.part_m, a.part_s, a.Mpad)
-  if (!a.vec) CCE_FWD(false, false);
-  else if (a.D % BK != 0) CCE_FWD(true, true);
-  else CCE_FWD(true, false);
+#define CCE_FWD(VEC, KT, CAP)                                                                   \
+  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL, CAP>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, \
+                     a.D, a.nMt, S, T, t0, t1, slot0, nl, a.softcap, a.part_m, a.part_s, a.Mpad)
+  const bool cap = a.softcap > 0.f;
+  if (!a.vec) {
+    if (cap) CCE_FWD(false, false, true); else CCE_FWD(false, false, false);
+  } else if (a.D % BK != 0) {
+    if (cap) CCE_FWD(true, true, true); else CCE_FWD(true, true, false);
+  } else {
+    if (cap) CCE_FWD(true, false, true); else CCE_FWD(true, false, false);
+  }
 #undef CCE_FWD
 }
 
@@ -194,7 +214,7 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_target_logit, dim3((a.M + 3) / 4), dim3(256), 0, st, a.H, a.W, a.y, a.M, a.V,
-                     a.D, a.tgt);
+                     a.D, a.softcap, a.tgt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, a.part_m, a.part_s,
                      a.tgt, a.y, a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status);

@@ -23,6 +23,7 @@ struct FwdArgs {
   int M, V, D;
   int nMt, nVt, S, T, Mpad;
   bool vec;
+  float softcap;  // 0: off; else logits are softcap * tanh(z / softcap)
   float* part_m;
   float* part_s;
   float* tgt;
@@ -56,6 +57,7 @@ struct BwdArgs {
   int M, V, D;
   int nMt, Mpad, Dpad, Vc;
   bool vec;
+  float softcap;  // as in FwdArgs
   float filter_eps, block_eps;
   float* dh;
   float* dW;

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert B.load().cce_abi_version() == 1
+    assert B.load().cce_abi_version() == 2
 
 
 def test_status_strings():
@@ -71,20 +71,25 @@ FAKE = 1 << 20   # a non-null pointer value; never dereferenced on these paths
 def test_forward_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    ok = (FAKE, FAKE, FAKE, 300, 1000, 64, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
-    for i in (0, 1, 2, 6, 7, 8, 9):
+    # h, W, y, M, V, D, softcap, logp, lse, dev_status, ws, ws_bytes, stream
+    ok = (FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    for i in (0, 1, 2, 7, 8, 9, 10):
         args = list(ok)
         args[i] = None
+        assert lib.cce_forward(*args) == B.CCE_EINVAL
+    for bad in (-1.0, float("nan"), float("inf")):
+        args = list(ok)
+        args[6] = bad
         assert lib.cce_forward(*args) == B.CCE_EINVAL
     for i in (3, 4, 5):
         args = list(ok)
         args[i] = 0
         assert lib.cce_forward(*args) == B.CCE_ESHAPE
     args = list(ok)
-    args[10] = ws - 1
+    args[11] = ws - 1
     assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
     args = list(ok)
-    args[9] = FAKE * 256 + 16          # misaligned workspace
+    args[10] = FAKE * 256 + 16          # misaligned workspace
     assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
 
 
@@ -109,16 +114,18 @@ def test_epilogue_argument_errors():
 def test_backward_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None]
-    a = list(ok); a[8] = -1.0
-    assert lib.cce_backward(*a) == B.CCE_EINVAL
-    a = list(ok); a[9] = float("inf")
-    assert lib.cce_backward(*a) == B.CCE_EINVAL
-    a = list(ok); a[11] = None
+    # h, W, y, lse, coef, M, V, D, softcap, filter_eps, block_eps, dh, dW, dev_status, ws,
+    # ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, 0.0, 0.0, FAKE, FAKE, FAKE, FAKE * 256,
+          ws, None]
+    for i, bad in ((8, -1.0), (8, float("nan")), (9, -1.0), (10, float("inf"))):
+        a = list(ok); a[i] = bad
+        assert lib.cce_backward(*a) == B.CCE_EINVAL
+    a = list(ok); a[12] = None
     assert lib.cce_backward(*a) == B.CCE_EINVAL
     a = list(ok); a[7] = -3
     assert lib.cce_backward(*a) == B.CCE_ESHAPE
-    a = list(ok); a[14] = 1
+    a = list(ok); a[15] = 1
     assert lib.cce_backward(*a) == B.CCE_EWORKSPACE
 
 
@@ -133,5 +140,5 @@ def test_valid_call_without_gfx950_is_refused():
         pass
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
     assert st == B.CCE_EDEVICE

@@ -37,13 +37,14 @@ def upload(wl, device):
     return h, W, y, seg
 
 
-def run_gpu(wl, device, filter_eps=0.0, block_eps=0.0, W_override=None):
+def run_gpu(wl, device, filter_eps=0.0, block_eps=0.0, W_override=None, softcap=0.0):
     head = B.Head(wl.M, wl.V, wl.D, device)
     h, W, y, seg = upload(wl, device)
     if W_override is not None:
         W = W_override
     head.clear_status()
-    out = B.step(head, h, W, y, seg, wl.n_pairs, wl.lam, wl.scope, filter_eps, block_eps)
+    out = B.step(head, h, W, y, seg, wl.n_pairs, wl.lam, wl.scope, filter_eps, block_eps,
+                 softcap=softcap)
     torch.cuda.synchronize()
     status = head.read_status()
     res = {k: v.detach().cpu().numpy() for k, v in out.items()}
@@ -232,29 +233,29 @@ def test_run_to_run_bytes_identical(device):
 # full-size configs in the benchmark's launch configuration: sampled rows,
 # closed forms and invariants (the full fp64 oracle would take minutes)
 # ----------------------------------------------------------------------------
-def _sampled_full_size(name, device, n_rows=24):
+def _sampled_full_size(name, device, n_rows=24, softcap=0.0):
     wl = WL.make_workload(name)
-    say(f"[gpu] {name} full size M={wl.M} V={wl.V} D={wl.D}: sampled rows")
+    say(f"[gpu] {name} full size M={wl.M} V={wl.V} D={wl.D} softcap={softcap}: sampled rows")
     head = B.Head(wl.M, wl.V, wl.D, device)
     h, W, y, seg = upload(wl, device)
     head.clear_status()
-    logp, lse = head.forward(h, W, y)
+    logp, lse = head.forward(h, W, y, softcap=softcap)
     # backward with a seeded coefficient (an input here, drawn like the others)
     rng = np.random.default_rng(np.random.SeedSequence([WL.BASE_SEED, 77]))
     coef = (rng.standard_normal(wl.M) * 1e-4).astype(np.float32)
     coef[wl.y < 0] = 0.0
-    dh, dW = head.backward(h, W, y, lse, torch.from_numpy(coef).to(device))
+    dh, dW = head.backward(h, W, y, lse, torch.from_numpy(coef).to(device), softcap=softcap)
     torch.cuda.synchronize()
     assert head.read_status() == 0
     rows = np.sort(rng.choice(wl.M, size=n_rows, replace=False))
     H64 = WL.bf16_bits_to_f32(wl.h_bits[rows]).astype(np.float64)
     W64 = wl.W64()
-    lp_o, lse_o = O.forward(H64, W64, wl.y[rows])
+    lp_o, lse_o = O.forward(H64, W64, wl.y[rows], softcap)
     ok = wl.y[rows] >= 0
     check_rows(logp.cpu().numpy()[rows][ok], lp_o[ok], f"{name} logp")
     check_rows(lse.cpu().numpy()[rows], lse_o, f"{name} lse")
     dh_o = O.backward_dh_rows(H64, W64, wl.y[rows], lse_o, coef[rows].astype(np.float64),
-                              np.arange(n_rows))
+                              np.arange(n_rows), softcap=softcap)
     dh_g = dh.cpu().numpy()[rows]
     nzr = coef[rows] != 0
     e = rel_l2(dh_g[nzr], dh_o[nzr])
@@ -333,3 +334,41 @@ def test_full_size_sampled(device, name):
 @pytest.mark.parametrize("name", ["gemma4b_head"])
 def test_full_size_zero_head(device, name):
     _zero_head_full_size(name, device)
+
+
+# ----------------------------------------------------------------------------
+# final-logit softcap: cap * tanh(z / cap) in the forward, sech^2 in the
+# backward ("Training — design …" §5.1, the e4b head; "ORPO training —
+# design", lever 1 spec).  Caps are chosen so that tanh is far from linear on
+# these logits (raw logit scale several times the cap in the first cases).
+# ----------------------------------------------------------------------------
+SOFTCAP = [
+    # spans, D, V, targets, hidden_scale, w_std, cap, filter/block eps
+    ([(31, 128, 128)], 256, 4096, "uniform", 3.0, 0.3, 5.0, 0.0),            # cap binds hard
+    ([(5, 30, 30, 5)], 77, 1000, "uniform", 2.0, 0.4, 2.0, 0.0),             # D % 8 != 0: slow loads
+    ([(100, 250, 240, 10)], 128, 33000, "zipf", 2.0, 0.2, 3.0, 0.0),         # 3 chunks, ragged V
+    ([(20, 100, 90, 4), (3, 40, 50)], 192, 20000, "zipf", 4.0, 0.25, 8.0, 1e-6),  # filter + block skip
+]
+
+
+@pytest.mark.parametrize("case", range(len(SOFTCAP)))
+def test_softcap_full(device, case):
+    spans, D, V, tg, hs, ws, cap, eps = SOFTCAP[case]
+    wl = WL.make_custom(spans, D=D, V=V, seed=300 + case, hidden_scale=hs, w_std=ws, targets=tg,
+                        lam=0.4, scope=WL.SCOPE_FULL)
+    say(f"[gpu] softcap case {case}: M={wl.M} V={wl.V} D={wl.D} cap={cap} eps={eps}")
+    g, st = run_gpu(wl, device, eps, eps, softcap=cap)
+    assert st == 0
+    o = O.step(wl.h64(), wl.W64(), wl.y, wl.seg, wl.n_pairs, wl.lam, wl.scope, filter_eps=eps,
+               softcap=cap)
+    check_full(wl, g, o, wl.scope, tag=f"softcap{case}")
+    if eps == 0.0:
+        # the same inputs without the cap differ clearly: the cap is really applied
+        o0 = O.forward(wl.h64(), wl.W64(), wl.y)[0]
+        valid = wl.y >= 0
+        assert np.max(np.abs(o0[valid] - o["logp"][valid])) > 1e-2
+
+
+def test_softcap_full_size_sampled(device):
+    """The Gemma-4B head at full size with the pages' e4b cap of 30."""
+    _sampled_full_size("gemma4b_head", device, softcap=30.0)
