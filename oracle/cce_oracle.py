@@ -31,7 +31,14 @@ reason in the design notes of the repository):
   * the final-logit softcap is cap * tanh(z / cap) evaluated exactly (the pages'
     head divides by a bf16-rounded cap inside its framework's op; here the cap
     is a plain float argument), applied before both the log-sum-exp and the
-    target gather, with sech^2(z / cap) in the backward; cap = 0 means off.
+    target gather, with sech^2(z / cap) in the backward; cap = 0 means off;
+  * the preference objectives other than ORPO use s = beta (lw - lr) - gamma
+    (SimPO's margin gamma is not scaled by beta, as in the research-directions
+    page; the design page's softplus(-beta((lw - lr) - gamma)) is the same
+    family with gamma replaced by beta * gamma); IPO is the reference-free
+    (s)^2 on the length-normalised means; the hinge's derivative at its kink is
+    taken as 0; every member may add the NLL term with a weight (0 for pure
+    SimPO, 1 for ORPO and the gamma-hybrid).
 
 Every function here has a pin in the test-suite (closed forms, library special
 cases, finite differences, brute force, invariants); none is "parity unpinned"
@@ -262,6 +269,95 @@ def epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope:
 
 def loss_from_logp(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope: int) -> float:
     return epilogue(logp, seg, n_pairs, lam, scope)["loss"]
+
+
+# ----------------------------------------------------------------------------
+# Preference-objective family on the same per-pair means.  [P1] §8.3 "Objective
+# variants and data" (SimPO softplus(-beta((lw - lr) - gamma)), IPO, hinge /
+# SLiC margin) and "ORPO from-base on UltraFeedback (mixed-5bpw) — results +
+# research directions" §6.1 (SimPO: -log sigma(beta (lw - ll) - gamma), no SFT
+# term), §6.2 (the gamma-hybrid: NLL(chosen) + lambda [-log sigma(beta (lw -
+# ll) - gamma)]), §6.3 (SFT + SimPO in one stage).  Per pair b:
+#   s_b = log_odds_b                      (ORPO)
+#       = beta (lw_b - lr_b) - gamma      (SIGMOID, IPO, HINGE)
+#   P_b = softplus(-s_b)  (ORPO, SIGMOID)  = -log sigma(s_b)
+#       = s_b^2           (IPO: reference-free, length-normalised; beta = 1 and
+#                          gamma = 1/(2 tau) give IPO's (h - 1/(2 tau))^2)
+#       = max(0, -s_b)    (HINGE: max(0, gamma - beta (lw - lr)); derivative 0
+#                          at the kink)
+#   L = mean_b (w_nll NLL_b + lambda P_b),  NLL_b as in the ORPO epilogue.
+# ORPO with w_nll = 1 is exactly `epilogue` above.
+# ----------------------------------------------------------------------------
+OBJ_ORPO, OBJ_SIGMOID, OBJ_IPO, OBJ_HINGE = 0, 1, 2, 3
+
+
+def pref_term(objective: int, s: float) -> float:
+    if objective in (OBJ_ORPO, OBJ_SIGMOID):
+        return softplus(-s)
+    if objective == OBJ_IPO:
+        return s * s
+    if objective == OBJ_HINGE:
+        return max(0.0, -s)
+    raise ValueError(objective)
+
+
+def dpref_term(objective: int, s: float) -> float:
+    """dP/ds."""
+    if objective in (OBJ_ORPO, OBJ_SIGMOID):
+        return -(1.0 - sigmoid(s))
+    if objective == OBJ_IPO:
+        return 2.0 * s
+    if objective == OBJ_HINGE:
+        return -1.0 if s < 0.0 else 0.0
+    raise ValueError(objective)
+
+
+def pref_epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, objective: int,
+                  nll_weight: float, lam: float, beta: float, gamma: float, scope: int) -> Dict:
+    logp = np.asarray(logp, np.float64)
+    seg = np.asarray(seg, np.int64)
+    kind = seg & 3
+    pair = seg >> 2
+    B = int(n_pairs)
+    out = {k: np.zeros(B) for k in ("lw", "lr", "pm", "s", "pref_b", "nll_b")}
+    Mw = np.zeros(B, np.int64)
+    Mr = np.zeros(B, np.int64)
+    Pm1 = np.zeros(B, np.int64)
+    coef = np.zeros(logp.shape[0])
+    for b in range(B):
+        C = (pair == b) & (kind == KIND_CHOSEN)
+        R = (pair == b) & (kind == KIND_REJECTED)
+        Q = (pair == b) & (kind == KIND_PROMPT)
+        Mw[b], Mr[b], Pm1[b] = int(C.sum()), int(R.sum()), int(Q.sum())
+        if Mw[b] == 0 or Mr[b] == 0:
+            raise ValueError(f"pair {b} has an empty response span")
+        lw = logp[C].sum() / Mw[b]
+        lr = logp[R].sum() / Mr[b]
+        pm = logp[Q].sum() / Pm1[b] if Pm1[b] > 0 else 0.0
+        if objective == OBJ_ORPO:
+            s = log_odds(lw, lr)
+            ds_w, ds_r = 1.0 - dlog1mexp(lw), -1.0 + dlog1mexp(lr)
+        else:
+            s = beta * (lw - lr) - gamma
+            ds_w, ds_r = beta, -beta
+        nll_b = full_nll(pm, int(Pm1[b]), lw, int(Mw[b])) if scope == SCOPE_FULL else -lw
+        for k, v in (("lw", lw), ("lr", lr), ("pm", pm), ("s", s),
+                     ("pref_b", pref_term(objective, s)), ("nll_b", nll_b)):
+            out[k][b] = v
+        # coef_i = -dL/dlogp_i
+        dP = dpref_term(objective, s)
+        if scope == SCOPE_FULL:
+            w = nll_weight / (Pm1[b] + Mw[b])
+            coef[Q] = w / B
+        else:
+            w = nll_weight / Mw[b]
+        coef[C] = (w - lam * dP * ds_w / Mw[b]) / B
+        coef[R] = (-lam * dP * ds_r / Mr[b]) / B
+    nll = out["nll_b"].mean()
+    pref = out["pref_b"].mean()
+    return dict(loss=nll_weight * nll + lam * pref, nll=nll, pref=pref, margin=out["s"].mean(),
+                accuracy=float(np.mean(out["lw"] > out["lr"])), Mw=Mw, Mr=Mr, Pm1=Pm1,
+                coef=coef, **out)
 
 
 # ----------------------------------------------------------------------------

@@ -612,3 +612,98 @@ def test_p10_softcap_finite_differences():
     onehot[np.nonzero(y >= 0)[0], y[y >= 0]] = 1.0
     dh_nosech = (ep["coef"][:, None] * (np.exp(Zc - lse[:, None]) - onehot)) @ W
     assert np.linalg.norm(dh_nosech - fdH) / np.linalg.norm(fdH) > 1e-2
+
+
+# ----------------------------------------------------------------------------
+# P11: the preference-objective family ([P1] §8.3; "ORPO from-base on
+# UltraFeedback — results + research directions" §6.1-6.3)
+# ----------------------------------------------------------------------------
+OBJECTIVES = [O.OBJ_ORPO, O.OBJ_SIGMOID, O.OBJ_IPO, O.OBJ_HINGE]
+
+
+def test_p11_orpo_member_is_the_orpo_epilogue():
+    seg = WL.layout_pairs([(2, 3, 2, 1), (1, 2, 3), (0, 4, 2)])
+    rng = np.random.default_rng(31)
+    logp = -rng.uniform(0.3, 4.0, size=seg.shape[0])
+    for scope in (O.SCOPE_FULL, O.SCOPE_RESPONSE):
+        a = O.epilogue(logp, seg, 3, 0.45, scope)
+        b = O.pref_epilogue(logp, seg, 3, O.OBJ_ORPO, 1.0, 0.45, 7.0, 9.0, scope)
+        assert b["loss"] == a["loss"] and b["nll"] == a["nll"] and b["pref"] == a["orv"]
+        assert b["margin"] == a["margin"] and b["accuracy"] == a["accuracy"]
+        np.testing.assert_array_equal(b["coef"], a["coef"])
+        np.testing.assert_array_equal(b["s"], a["log_odds"])
+
+
+def _dec_softplus_neg(x):
+    """softplus(-x) = log(1 + e^-x) in 50-digit decimal arithmetic."""
+    getcontext().prec = 50
+    return float((Decimal(1) + (-Decimal(x)).exp()).ln())
+
+
+@pytest.mark.parametrize("lw,lr,beta,gamma", [(-1.2, -1.5, 2.0, 0.5), (-3.0, -2.1, 0.7, 0.1),
+                                               (-0.4, -0.4, 3.0, 0.0)])
+def test_p11_closed_forms_one_pair(lw, lr, beta, gamma):
+    """One pair, one chosen and one rejected row, response scope: every term
+    evaluated independently by hand (decimal arithmetic for the softplus)."""
+    seg = WL.layout_pairs([(0, 1, 1)])
+    logp = np.array([lw, lr])
+    s = beta * (lw - lr) - gamma
+    want = {O.OBJ_SIGMOID: _dec_softplus_neg(s), O.OBJ_IPO: s * s, O.OBJ_HINGE: max(0.0, gamma - beta * (lw - lr))}
+    for obj, P in want.items():
+        for w_nll, lam in ((0.0, 1.0), (1.0, 0.3)):
+            ep = O.pref_epilogue(logp, seg, 1, obj, w_nll, lam, beta, gamma, O.SCOPE_RESPONSE)
+            assert ep["pref"] == pytest.approx(P, rel=1e-14, abs=1e-15)
+            assert ep["loss"] == pytest.approx(w_nll * (-lw) + lam * P, rel=1e-14, abs=1e-15)
+            assert ep["margin"] == pytest.approx(s, rel=1e-15, abs=1e-15)
+
+
+@pytest.mark.parametrize("objective", OBJECTIVES)
+def test_p11_finite_differences_of_coef(objective):
+    """coef_i = -dL/dlogp_i for every member, by central differences."""
+    seg = WL.layout_pairs([(2, 3, 2, 1), (1, 2, 3)])
+    rng = np.random.default_rng(40 + objective)
+    logp = -rng.uniform(0.3, 4.0, size=seg.shape[0])
+    for scope in (O.SCOPE_FULL, O.SCOPE_RESPONSE):
+        for w_nll, lam, beta, gamma in ((1.0, 0.6, 1.7, 0.3), (0.0, 1.0, 2.5, -0.4)):
+            def L(lp):
+                return O.pref_epilogue(lp, seg, 2, objective, w_nll, lam, beta, gamma, scope)["loss"]
+            ep = O.pref_epilogue(logp, seg, 2, objective, w_nll, lam, beta, gamma, scope)
+            for i in range(len(logp)):
+                e = 1e-6
+                lp, lm = logp.copy(), logp.copy()
+                lp[i] += e
+                lm[i] -= e
+                fd = (L(lp) - L(lm)) / (2 * e)
+                assert -fd == pytest.approx(ep["coef"][i], rel=1e-6, abs=1e-9), (scope, i)
+
+
+def test_p11_gamma_hybrid_torch_autograd():
+    """The gamma-hybrid (NLL + lambda * -log sigmoid(beta (lw - lr) - gamma))
+    through torch fp64 autograd, from H and W to the loss, against the oracle's
+    forward, coefficients and analytic backward."""
+    torch = pytest.importorskip("torch")
+    spans = [(4, 6, 5, 1), (0, 3, 4), (2, 5, 5, 3)]
+    wl = WL.make_custom(spans, D=16, V=29, seed=55, hidden_scale=1.5, w_std=0.4, lam=0.7)
+    H, W, y, seg = wl.h64(), wl.W64(), wl.y, wl.seg
+    kind, pair = seg & 3, seg >> 2
+    beta, gamma, lam = 2.0, 0.25, 0.7
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    lsm = torch.log_softmax(Ht @ Wt.T, dim=1)
+    lp = lsm[torch.arange(len(y)), torch.tensor(np.maximum(y, 0))] * torch.tensor(y >= 0)
+    terms = []
+    for b in range(len(spans)):
+        C = torch.tensor((pair == b) & (kind == WL.KIND_CHOSEN))
+        R = torch.tensor((pair == b) & (kind == WL.KIND_REJECTED))
+        Q = torch.tensor((pair == b) & (kind == WL.KIND_PROMPT))
+        lw, lr = lp[C].mean(), lp[R].mean()
+        nll = -(lp[Q].sum() + lp[C].sum()) / (int(Q.sum()) + int(C.sum()))
+        terms.append(nll - lam * torch.nn.functional.logsigmoid(beta * (lw - lr) - gamma))
+    loss = torch.stack(terms).mean()
+    loss.backward()
+    logp, lse = O.forward(H, W, y)
+    ep = O.pref_epilogue(logp, seg, len(spans), O.OBJ_SIGMOID, 1.0, lam, beta, gamma, O.SCOPE_FULL)
+    assert ep["loss"] == pytest.approx(loss.item(), rel=1e-12)
+    dh, dW = O.backward(H, W, y, lse, ep["coef"])
+    np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
