@@ -128,6 +128,37 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
                          float* out5, float* pair_stats, float* coef,
                          uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
 
+/* Preference objectives of pref_epilogue. */
+enum { CCE_OBJ_ORPO = 0, CCE_OBJ_SIGMOID = 1, CCE_OBJ_IPO = 2, CCE_OBJ_HINGE = 3 };
+
+/*
+ * Preference-objective epilogue: the ORPO epilogue's family on the same
+ * per-pair means lw, lr, pm and NLL_b ("Training — design …" §8.3 "Objective
+ * variants and data"; "ORPO from-base on UltraFeedback (mixed-5bpw) — results
+ * + research directions" §6.1 SimPO, §6.2 the gamma-hybrid, §6.3):
+ *   s_b = log_odds_b (CCE_OBJ_ORPO)  or  beta (lw - lr) - gamma (the others);
+ *   P_b = softplus(-s_b) = -log sigmoid(s_b)   (CCE_OBJ_ORPO, CCE_OBJ_SIGMOID)
+ *       = s_b^2                                (CCE_OBJ_IPO; beta = 1 and
+ *                                               gamma = 1/(2 tau) give IPO)
+ *       = max(0, -s_b)                         (CCE_OBJ_HINGE; derivative 0 at
+ *                                               the kink);
+ *   loss = mean_b (nll_weight NLL_b + lambda P_b).
+ * SimPO is CCE_OBJ_SIGMOID with nll_weight 0 and lambda 1; the gamma-hybrid is
+ * CCE_OBJ_SIGMOID with nll_weight 1; orpo_epilogue is CCE_OBJ_ORPO with
+ * nll_weight 1 (beta, gamma unused).
+ *   Arguments as for orpo_epilogue, plus objective (CCE_OBJ_*), nll_weight,
+ *   beta, gamma (finite, else CCE_EINVAL).
+ *   out5 [5]: loss, nll (mean NLL_b), pref (mean P_b), margin (mean s_b),
+ *             accuracy (fraction of pairs with lw > lr).
+ *   pair_stats [n_pairs, 8] (may be NULL): lw, lr, s_b, NLL_b, P_b, Mw, Mr, P-1.
+ *   coef [M]: -dloss/dlogp_i, as for orpo_epilogue.
+ */
+cce_status pref_epilogue(const float* logp, const int32_t* y, const int32_t* seg,
+                         int64_t M, int32_t n_pairs, int objective, float nll_weight,
+                         float lambda, float beta, float gamma, int scope,
+                         float* out5, float* pair_stats, float* coef,
+                         uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * Backward of the head given the per-row coefficient coef_i = -dL/dlogp_i:
  *   G_{i,v} = coef_i (softmax_{i,v} - [v = y_i]) s_{i,v},  dh = G W,  dW = G^T h,

@@ -20,6 +20,7 @@ CCE_OK, CCE_EINVAL, CCE_ESHAPE, CCE_EWORKSPACE, CCE_EDEVICE, CCE_ELAUNCH = range
 KIND_IGNORE, KIND_PROMPT, KIND_CHOSEN, KIND_REJECTED = 0, 1, 2, 3
 SCOPE_FULL, SCOPE_RESPONSE = 0, 1
 DERR_TARGET, DERR_PAIR, DERR_EMPTY_SPAN, DERR_NONFINITE = 1, 2, 4, 8
+OBJ_ORPO, OBJ_SIGMOID, OBJ_IPO, OBJ_HINGE = 0, 1, 2, 3
 
 # exported symbols and their C signatures (kept in step with include/flashcce.h)
 _c_i64, _c_f, _c_p, _c_sz, _c_i = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -33,6 +34,8 @@ SIGNATURES = {
                              _c_p, _c_p, _c_sz, _c_p]),
     "cce_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_f, _c_f,
                             _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "pref_epilogue": (_c_i, [_c_p, _c_p, _c_p, _c_i64, ctypes.c_int32, _c_i, _c_f, _c_f, _c_f, _c_f,
+                             _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
 }
 
 _lib = None
@@ -161,6 +164,29 @@ class Head:
                                   _dev(coef, "coef", torch.float32, (M,)),
                                   self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
         _check("orpo_epilogue", st)
+        return out5, pair_stats, coef
+
+    # -- preference-objective epilogue ----------------------------------------
+    def pref_epilogue(self, logp, y, seg, n_pairs: int, objective: int, nll_weight: float,
+                      lam: float, beta: float, gamma: float, scope: int,
+                      out5=None, pair_stats=None, coef=None, stream=None):
+        M = self.M
+        if out5 is None:
+            out5 = torch.empty(5, dtype=torch.float32, device=self.device)
+        if pair_stats is None:
+            pair_stats = torch.empty((n_pairs, 8), dtype=torch.float32, device=self.device)
+        if coef is None:
+            coef = torch.empty(M, dtype=torch.float32, device=self.device)
+        st = load().pref_epilogue(_dev(logp, "logp", torch.float32, (M,)),
+                                  _dev(y, "y", torch.int32, (M,)),
+                                  _dev(seg, "seg", torch.int32, (M,)), M, int(n_pairs),
+                                  int(objective), float(nll_weight), float(lam), float(beta),
+                                  float(gamma), int(scope),
+                                  _dev(out5, "out5", torch.float32, (5,)),
+                                  _dev(pair_stats, "pair_stats", torch.float32, (n_pairs, 8)),
+                                  _dev(coef, "coef", torch.float32, (M,)),
+                                  self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
+        _check("pref_epilogue", st)
         return out5, pair_stats, coef
 
     # -- backward -------------------------------------------------------------

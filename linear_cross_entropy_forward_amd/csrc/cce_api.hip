@@ -97,7 +97,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int cce_abi_version(void) { return 2; }
+int cce_abi_version(void) { return 3; }
 
 const char* cce_status_string(int status) {
   switch (status) {
@@ -151,13 +151,17 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
                                                                                : CCE_ELAUNCH;
 }
 
-cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg, int64_t M,
-                         int32_t n_pairs, float lambda, int scope, float* out5, float* pair_stats,
-                         float* coef, uint32_t* dev_status, void* ws, size_t ws_bytes,
-                         void* stream) {
+// Both epilogue entry points: argument checks, then the same kernels.
+static cce_status epilogue_common(const float* logp, const int32_t* y, const int32_t* seg,
+                                  int64_t M, int32_t n_pairs, int objective, float nll_weight,
+                                  float lambda, float beta, float gamma, int scope, float* out5,
+                                  float* pair_stats, float* coef, uint32_t* dev_status, void* ws,
+                                  size_t ws_bytes, void* stream) {
   if (!logp || !y || !seg || !out5 || !coef || !dev_status || !ws) return CCE_EINVAL;
   if (scope != CCE_SCOPE_FULL && scope != CCE_SCOPE_RESPONSE) return CCE_EINVAL;
-  if (!isfinite(lambda)) return CCE_EINVAL;
+  if (objective < CCE_OBJ_ORPO || objective > CCE_OBJ_HINGE) return CCE_EINVAL;
+  if (!isfinite(lambda) || !isfinite(nll_weight) || !isfinite(beta) || !isfinite(gamma))
+    return CCE_EINVAL;
   if (M < 1 || M > kMaxM || n_pairs < 1 || (int64_t)n_pairs > M) return CCE_ESHAPE;
   // the epilogue's part of the workspace depends on M only; any V, D >= 1 give it
   const Layout L = layout(M, 1, 1);
@@ -172,7 +176,11 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
   a.seg = seg;
   a.M = (int)M;
   a.n_pairs = n_pairs;
+  a.objective = objective;
+  a.nll_weight = (double)nll_weight;
   a.lambda = (double)lambda;
+  a.beta = (double)beta;
+  a.gamma = (double)gamma;
   a.scope = scope;
   a.pairs = reinterpret_cast<double*>(static_cast<char*>(ws) + L.pairs);
   a.out5 = out5;
@@ -181,6 +189,23 @@ cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg
   a.status = dev_status;
   return cce::launch_epilogue(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
+}
+
+cce_status orpo_epilogue(const float* logp, const int32_t* y, const int32_t* seg, int64_t M,
+                         int32_t n_pairs, float lambda, int scope, float* out5, float* pair_stats,
+                         float* coef, uint32_t* dev_status, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return epilogue_common(logp, y, seg, M, n_pairs, CCE_OBJ_ORPO, 1.f, lambda, 0.f, 0.f, scope,
+                         out5, pair_stats, coef, dev_status, ws, ws_bytes, stream);
+}
+
+cce_status pref_epilogue(const float* logp, const int32_t* y, const int32_t* seg, int64_t M,
+                         int32_t n_pairs, int objective, float nll_weight, float lambda,
+                         float beta, float gamma, int scope, float* out5, float* pair_stats,
+                         float* coef, uint32_t* dev_status, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return epilogue_common(logp, y, seg, M, n_pairs, objective, nll_weight, lambda, beta, gamma,
+                         scope, out5, pair_stats, coef, dev_status, ws, ws_bytes, stream);
 }
 
 cce_status cce_backward(const void* h, const void* W, const int32_t* y, const float* lse,

@@ -10,6 +10,14 @@
 // 1/(1 - e^l) factor of the OR gradient ("ORPO training — design",
 // "Recommended defaults") enters through d log_odds / d l.
 //
+// The same kernels serve the preference-objective family ("Training — design
+// …" §8.3 "Objective variants and data"; "ORPO from-base on UltraFeedback —
+// results + research directions" §6.1-6.3): per pair a separation
+//   s = log_odds (ORPO)  or  s = beta (lw - lr) - gamma (the others),
+// a preference term P(s) = softplus(-s) (ORPO, sigmoid / SimPO), s^2 (IPO) or
+// max(0, -s) (hinge, derivative 0 at the kink), and
+//   L = mean_b (nll_weight NLL_b + lambda P_b).
+//
 // Three small kernels: per-pair sums (one workgroup per pair, fixed-order fp64
 // tree reduction), batch means (one workgroup), per-row coefficients.
 #include <math.h>
@@ -41,8 +49,10 @@ __device__ double sigmoid_d(double x) {
 __global__ __launch_bounds__(256) void k_epi_pairs(const float* __restrict__ logp,
                                                    const int* __restrict__ y,
                                                    const int* __restrict__ seg, int M, int B,
-                                                   double lambda, int scope,
-                                                   double* __restrict__ pairs, unsigned* status) {
+                                                   int objective, double nll_weight,
+                                                   double lambda, double beta, double gamma,
+                                                   int scope, double* __restrict__ pairs,
+                                                   unsigned* status) {
   __shared__ double sh[3][256];
   __shared__ int shn[3][256];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -108,18 +118,35 @@ __global__ __launch_bounds__(256) void k_epi_pairs(const float* __restrict__ log
     return;
   }
   const double lw = sc / nc, lr = sr / nr, pm = np > 0 ? sp / np : 0.0;
-  const double lo = (lw - lr) - (log1mexp_d(lw) - log1mexp_d(lr));
-  const double sig = sigmoid_d(lo);
+  double sep, ds_w, ds_r;  // separation and its derivatives by lw, lr
+  if (objective == 0) {
+    sep = (lw - lr) - (log1mexp_d(lw) - log1mexp_d(lr));
+    ds_w = 1.0 - dlog1mexp_d(lw);
+    ds_r = -1.0 + dlog1mexp_d(lr);
+  } else {
+    sep = beta * (lw - lr) - gamma;
+    ds_w = beta;
+    ds_r = -beta;
+  }
+  double pref, dpref;  // preference term and dP/ds
+  if (objective == 2) {
+    pref = sep * sep;
+    dpref = 2.0 * sep;
+  } else if (objective == 3) {
+    pref = fmax(0.0, -sep);
+    dpref = sep < 0.0 ? -1.0 : 0.0;
+  } else {
+    pref = softplus_d(-sep);
+    dpref = -(1.0 - sigmoid_d(sep));
+  }
   const double nll = scope == 0 ? -((np > 0 ? np * pm : 0.0) + nc * lw) / (double)(np + nc) : -lw;
-  const double dlo_w = 1.0 - dlog1mexp_d(lw);
-  const double dlo_r = -1.0 + dlog1mexp_d(lr);
-  const double w_or = lambda * (1.0 - sig);
-  const double w_nll = scope == 0 ? 1.0 / (double)(np + nc) : 1.0 / (double)nc;
-  P[P_LW] = lw; P[P_LR] = lr; P[P_PM] = pm; P[P_LO] = lo;
-  P[P_OR] = softplus_d(-lo);
+  const double w_nll = nll_weight * (scope == 0 ? 1.0 / (double)(np + nc) : 1.0 / (double)nc);
+  const double w_pref = -lambda * dpref;  // -dL_b/ds (before 1/B)
+  P[P_LW] = lw; P[P_LR] = lr; P[P_PM] = pm; P[P_LO] = sep;
+  P[P_OR] = pref;
   P[P_NLL] = nll;
-  P[P_CC] = (w_nll + w_or * dlo_w / nc) / B;
-  P[P_CR] = (w_or * dlo_r / nr) / B;
+  P[P_CC] = (w_nll + w_pref * ds_w / nc) / B;
+  P[P_CR] = (w_pref * ds_r / nr) / B;
   P[P_CP] = scope == 0 ? w_nll / B : 0.0;
   P[P_ACC] = lw > lr ? 1.0 : 0.0;
   P[P_NC] = nc; P[P_NR] = nr; P[P_NP] = np;
@@ -127,7 +154,8 @@ __global__ __launch_bounds__(256) void k_epi_pairs(const float* __restrict__ log
 }
 
 __global__ __launch_bounds__(256) void k_epi_final(const double* __restrict__ pairs, int B,
-                                                   double lambda, float* __restrict__ out5,
+                                                   double nll_weight, double lambda,
+                                                   float* __restrict__ out5,
                                                    float* __restrict__ pair_stats,
                                                    unsigned* status) {
   __shared__ double sh[4][256];
@@ -159,7 +187,7 @@ __global__ __launch_bounds__(256) void k_epi_final(const double* __restrict__ pa
   }
   if (tid == 0) {
     const double nll = sh[0][0] / B, orv = sh[1][0] / B;
-    const double loss = nll + lambda * orv;
+    const double loss = nll_weight * nll + lambda * orv;
     out5[0] = (float)loss;
     out5[1] = (float)nll;
     out5[2] = (float)orv;
@@ -186,11 +214,12 @@ __global__ __launch_bounds__(256) void k_epi_coef(const int* __restrict__ seg,
 
 hipError_t launch_epilogue(const EpiArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_epi_pairs, dim3(a.n_pairs), dim3(256), 0, st, a.logp, a.y, a.seg, a.M,
-                     a.n_pairs, a.lambda, a.scope, a.pairs, a.status);
+                     a.n_pairs, a.objective, a.nll_weight, a.lambda, a.beta, a.gamma, a.scope,
+                     a.pairs, a.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_epi_final, dim3(1), dim3(256), 0, st, a.pairs, a.n_pairs, a.lambda, a.out5,
-                     a.pair_stats, a.status);
+  hipLaunchKernelGGL(k_epi_final, dim3(1), dim3(256), 0, st, a.pairs, a.n_pairs, a.nll_weight,
+                     a.lambda, a.out5, a.pair_stats, a.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_epi_coef, dim3((a.M + 255) / 256), dim3(256), 0, st, a.seg, a.pairs, a.M,

@@ -38,7 +38,10 @@ struct EpiArgs {
   const int* y;
   const int* seg;
   int M, n_pairs;
-  double lambda;
+  int objective;        // 0 ORPO, 1 sigmoid (SimPO), 2 IPO, 3 hinge
+  double nll_weight;    // weight of the NLL term (1 for ORPO)
+  double lambda;        // weight of the preference term
+  double beta, gamma;   // s = beta (lw - lr) - gamma (objectives other than ORPO)
   int scope;
   double* pairs;  // [n_pairs, kPairStride]
   float* out5;

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == {"cce_abi_version", "cce_status_string", "cce_workspace_bytes", "cce_forward",
-                     "orpo_epilogue", "cce_backward"}
+                     "orpo_epilogue", "pref_epilogue", "cce_backward"}
     assert names == set(B.SIGNATURES)
 
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert B.load().cce_abi_version() == 2
+    assert B.load().cce_abi_version() == 3
 
 
 def test_status_strings():
@@ -109,6 +109,23 @@ def test_epilogue_argument_errors():
     assert lib.orpo_epilogue(*a) == B.CCE_EINVAL
     a = list(ok); a[12] = 10
     assert lib.orpo_epilogue(*a) == B.CCE_EWORKSPACE
+
+
+def test_pref_epilogue_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes(300, 1, 1)
+    # logp, y, seg, M, n_pairs, objective, nll_weight, lambda, beta, gamma, scope, out5,
+    # pair_stats, coef, dev_status, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, 300, 2, 1, 1.0, 0.1, 2.0, 0.5, 0, FAKE, None, FAKE, FAKE, FAKE * 256, ws,
+          None]
+    for i, bad in ((5, -1), (5, 4), (10, 2), (6, float("nan")), (7, float("inf")), (8, float("nan")),
+                   (9, float("-inf")), (0, None), (13, None)):
+        a = list(ok); a[i] = bad
+        assert lib.pref_epilogue(*a) == B.CCE_EINVAL, (i, bad)
+    a = list(ok); a[4] = 301
+    assert lib.pref_epilogue(*a) == B.CCE_ESHAPE
+    a = list(ok); a[16] = 10
+    assert lib.pref_epilogue(*a) == B.CCE_EWORKSPACE
 
 
 def test_backward_argument_errors():

@@ -372,3 +372,68 @@ def test_softcap_full(device, case):
 def test_softcap_full_size_sampled(device):
     """The Gemma-4B head at full size with the pages' e4b cap of 30."""
     _sampled_full_size("gemma4b_head", device, softcap=30.0)
+
+
+# ----------------------------------------------------------------------------
+# preference-objective epilogue ("Training — design …" §8.3; "ORPO from-base
+# on UltraFeedback — results + research directions" §6.1-6.3)
+# ----------------------------------------------------------------------------
+PREF = [
+    # objective, nll_weight, lambda, beta, gamma, scope
+    (B.OBJ_SIGMOID, 0.0, 1.0, 2.0, 0.5, WL.SCOPE_RESPONSE),   # SimPO
+    (B.OBJ_SIGMOID, 1.0, 0.3, 2.5, 1.0, WL.SCOPE_FULL),       # gamma-hybrid
+    (B.OBJ_IPO, 0.0, 1.0, 1.0, 0.25, WL.SCOPE_RESPONSE),      # IPO, tau = 2
+    (B.OBJ_HINGE, 1.0, 0.5, 1.5, 0.2, WL.SCOPE_FULL),         # hinge + NLL
+    (B.OBJ_ORPO, 0.5, 0.2, 0.0, 0.0, WL.SCOPE_FULL),          # ORPO with a half NLL weight
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREF)))
+def test_pref_epilogue_full(device, case):
+    obj, w_nll, lam, beta, gamma, scope = PREF[case]
+    spans = [(13, 40, 37, 5), (0, 21, 19), (7, 3, 9, 2), (4, 17, 22, 1)]
+    wl = WL.make_custom(spans, D=200, V=9000, seed=400 + case, hidden_scale=1.5, w_std=0.1,
+                        targets="zipf", lam=lam, scope=scope)
+    say(f"[gpu] pref epilogue case {case}: objective {obj} M={wl.M} pairs={wl.n_pairs}")
+    head = B.Head(wl.M, wl.V, wl.D, device)
+    h, W, y, seg = upload(wl, device)
+    head.clear_status()
+    logp, lse = head.forward(h, W, y)
+    out5, ps, coef = head.pref_epilogue(logp, y, seg, wl.n_pairs, obj, w_nll, lam, beta, gamma, scope)
+    dh, dW = head.backward(h, W, y, lse, coef)
+    torch.cuda.synchronize()
+    assert head.read_status() == 0
+    H, Wm = wl.h64(), wl.W64()
+    lp_o, lse_o = O.forward(H, Wm, wl.y)
+    o = O.pref_epilogue(lp_o, wl.seg, wl.n_pairs, obj, w_nll, lam, beta, gamma, scope)
+    out5, ps, coef_g = out5.cpu().numpy(), ps.cpu().numpy(), coef.cpu().numpy()
+    for k, idx in (("loss", 0), ("nll", 1), ("pref", 2)):
+        assert abs(out5[idx] - o[k]) <= RTOL_SCALAR * max(abs(o[k]), 1e-3), (k, out5[idx], o[k])
+    assert abs(out5[3] - o["margin"]) <= 1e-3 * max(1.0, abs(o["margin"]))
+    if np.all(np.abs(o["lw"] - o["lr"]) > 1e-4):
+        assert out5[4] == pytest.approx(o["accuracy"], abs=1e-7)
+    np.testing.assert_allclose(ps[:, 2], o["s"], rtol=1e-3, atol=1e-4)
+    np.testing.assert_allclose(ps[:, 4], o["pref_b"], rtol=1e-3, atol=1e-5)
+    assert np.array_equal(ps[:, 5].astype(np.int64), o["Mw"])
+    nz = o["coef"] != 0
+    np.testing.assert_allclose(coef_g[nz], o["coef"][nz], rtol=RTOL_SCALAR)
+    assert np.all(coef_g[~nz] == 0.0)
+    dh_o, dW_o = O.backward(H, Wm, wl.y, lse_o, o["coef"])
+    e_dh, e_dW = rel_l2(dh.cpu().numpy(), dh_o), rel_l2(dW.cpu().numpy(), dW_o)
+    say(f"  pref{case} dh rel L2 {e_dh:.3e}  dW rel L2 {e_dW:.3e}")
+    assert e_dh <= RTOL_GRAD and e_dW <= RTOL_GRAD
+    del head, h, W, y, seg, logp, lse, dh, dW
+    torch.cuda.empty_cache()
+
+
+def test_orpo_epilogue_is_pref_orpo(device):
+    """orpo_epilogue and pref_epilogue(ORPO, nll_weight 1) give identical bytes."""
+    wl = WL.make_custom([(13, 40, 37, 5), (0, 21, 19)], D=64, V=3000, seed=450, lam=0.35)
+    head = B.Head(wl.M, wl.V, wl.D, device)
+    h, W, y, seg = upload(wl, device)
+    logp, _ = head.forward(h, W, y)
+    a = head.epilogue(logp, y, seg, wl.n_pairs, wl.lam, wl.scope)
+    b = head.pref_epilogue(logp, y, seg, wl.n_pairs, B.OBJ_ORPO, 1.0, wl.lam, 3.0, 1.0, wl.scope)
+    torch.cuda.synchronize()
+    for x, z in zip(a, b):
+        assert x.cpu().numpy().tobytes() == z.cpu().numpy().tobytes()
