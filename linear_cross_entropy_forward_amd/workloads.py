@@ -246,3 +246,45 @@ def make_custom(M_spans, D: int, V: int, seed: int, hidden_scale: float = 1.0,
     return Workload(name=f"custom_{seed}", M=M, D=D, V=V, h_bits=f32_to_bf16_bits(h),
                     W_bits=f32_to_bf16_bits(W), y=y, seg=seg, n_pairs=len(M_spans),
                     lam=lam, scope=scope)
+
+
+# ----------------------------------------------------------------------------
+# Quantised heads (input preparation): the affine group format of the pages'
+# head ("Training — design …" §5.1 and §5.6: 4/8-bit affine with per-group
+# scales and biases, one spec per head).  Per row v and group g of group_size
+# consecutive columns: a scale s and a bias b (bf16 bit patterns), codes
+# q in [0, 2^bits), packed little-endian into uint32 words along the row
+# (code j of a word in bits [bits*j, bits*j + bits)).  The head value the
+# codes stand for is s*q + b; computing it is the method's business, not this
+# module's.  Codes are chosen by rounding against the stored (bf16) s and b.
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class QuantHead:
+    bits: int
+    group_size: int
+    Wq: np.ndarray            # uint32 [V, D * bits / 32]
+    scale_bits: np.ndarray    # uint16 [V, D / group_size]  bf16
+    bias_bits: np.ndarray     # uint16 [V, D / group_size]  bf16
+
+
+def quantize_affine(W: np.ndarray, bits: int, group_size: int) -> QuantHead:
+    W = np.asarray(W, np.float64)
+    V, D = W.shape
+    assert bits in (4, 8) and D % group_size == 0 and (D * bits) % 32 == 0
+    G = D // group_size
+    Wg = W.reshape(V, G, group_size)
+    lo, hi = Wg.min(axis=2), Wg.max(axis=2)
+    levels = (1 << bits) - 1
+    scale = np.where(hi > lo, (hi - lo) / levels, 1.0)
+    s_bits = f32_to_bf16_bits(scale.astype(np.float32))
+    b_bits = f32_to_bf16_bits(lo.astype(np.float32))
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)
+    b = bf16_bits_to_f32(b_bits).astype(np.float64)
+    q = np.clip(np.rint((Wg - b[:, :, None]) / s[:, :, None]), 0, levels).astype(np.uint64)
+    q = q.reshape(V, D)
+    per = 32 // bits
+    words = np.zeros((V, D // per), np.uint64)
+    for j in range(per):
+        words |= q[:, j::per] << np.uint64(bits * j)
+    return QuantHead(bits=bits, group_size=group_size, Wq=words.astype(np.uint32),
+                     scale_bits=s_bits, bias_bits=b_bits)

@@ -88,6 +88,25 @@ def dcapped(Z: np.ndarray, softcap: float) -> np.ndarray:
     return 1.0 - t * t
 
 
+def dequantize(Wq: np.ndarray, scale: np.ndarray, bias: np.ndarray, bits: int,
+               group_size: int) -> np.ndarray:
+    """The affine-quantised head's values ([P1] §5.1 "in-Metal 4/8-bit affine
+    dequant", §5.6 "Quantized base"): W[v, d] = s[v, g] * q[v, d] + b[v, g] with
+    g = d // group_size, q the bits-wide code of column d, stored little-endian
+    in uint32 words along the row (code j of a word in bits bits*j ..).
+    scale and bias are the per-group values (any float dtype); fp64 result."""
+    Wq = np.asarray(Wq, np.uint64)
+    V = Wq.shape[0]
+    per = 32 // bits
+    D = Wq.shape[1] * per
+    q = np.empty((V, D), np.float64)
+    mask = np.uint64((1 << bits) - 1)
+    for j in range(per):
+        q[:, j::per] = ((Wq >> np.uint64(bits * j)) & mask).astype(np.float64)
+    g = np.arange(D) // group_size
+    return np.asarray(scale, np.float64)[:, g] * q + np.asarray(bias, np.float64)[:, g]
+
+
 def logsumexp_rows(Z: np.ndarray) -> np.ndarray:
     """log sum_v exp(Z[i, v]) with the row max factored out."""
     m = Z.max(axis=1)

@@ -707,3 +707,44 @@ def test_p11_gamma_hybrid_torch_autograd():
     dh, dW = O.backward(H, W, y, lse, ep["coef"])
     np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-10, atol=1e-15)
     np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# P12: the affine-quantised head ([P1] §5.1, §5.6)
+# ----------------------------------------------------------------------------
+def test_p12_dequantize_hand_example():
+    """4-bit codes 0..7 in one word (code j at bits 4j), then 15..8 in the next;
+    8-bit codes 1, 2, 3, 250 in one word; values by hand."""
+    Wq = np.array([[0x76543210, 0x89ABCDEF]], np.uint32)
+    W = O.dequantize(Wq, np.array([[2.0]]), np.array([[-1.0]]), 4, 16)
+    assert W.tolist() == [[-1.0, 1.0, 3.0, 5.0, 7.0, 9.0, 11.0, 13.0,
+                           29.0, 27.0, 25.0, 23.0, 21.0, 19.0, 17.0, 15.0]]
+    Wq8 = np.array([[0xFA030201]], np.uint32)
+    W8 = O.dequantize(Wq8, np.array([[0.5, 0.25]]), np.array([[1.0, -2.0]]), 8, 2)
+    assert W8.tolist() == [[1.5, 2.0, -1.25, 60.5]]
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 32), (8, 64), (8, 128)])
+def test_p12_dequantize_round_trip(bits, group):
+    """dequantize(quantize(W)) lies within half a code step (plus the bf16
+    rounding of the stored bias) of W, and reproduces the group extremes' span:
+    the quantiser (input preparation) and the oracle's dequantiser agree on
+    the format."""
+    rng = np.random.default_rng(bits * 1000 + group)
+    W = rng.standard_normal((37, 256)) * 0.05
+    qh = WL.quantize_affine(W, bits, group)
+    s = WL.bf16_bits_to_f32(qh.scale_bits).astype(np.float64)
+    b = WL.bf16_bits_to_f32(qh.bias_bits).astype(np.float64)
+    Wd = O.dequantize(qh.Wq, s, b, bits, group)
+    g = np.arange(256) // group
+    step = s[:, g]
+    err = np.abs(Wd - W)
+    # rounding to the nearest code: half a step, plus what bf16 rounding of the
+    # stored scale and bias shifts (the bias by its own rounding, the scale by
+    # up to 2^-8 relative times the largest code)
+    tol = 0.5 * step + np.abs(b[:, g]) * 2.0 ** -8 + step * 2.0 ** -8 * ((1 << bits) - 1) + 1e-12
+    assert np.all(err <= tol)
+    levels = (1 << bits) - 1
+    codes = np.rint((Wd - b[:, g]) / step)
+    assert codes.min() >= 0 and codes.max() <= levels
+    assert np.allclose(codes, (Wd - b[:, g]) / step, atol=1e-9)
