@@ -183,6 +183,47 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y,
                         float* dh, float* dW, uint32_t* dev_status,
                         void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Affine-quantised head (frozen): the forward and dh of the head when W is held
+ * as 4- or 8-bit codes with a bf16 scale and bias per row and group of
+ * group_size columns ("Training — design …" §5.1, the classifier is the
+ * quantised head, dequantised inside the kernel, frozen so only dh flows back;
+ * §5.6 "Quantized base", a vocab chunk is a row slice of the codes, scales and
+ * biases).  Element (v, d) of the head is
+ *     W[v, d] = s[v, d / group_size] * q[v, d] + b[v, d / group_size],
+ * q[v, d] the bits-bit code at bit offset bits * (d % (32 / bits)) of word
+ * d / (32 / bits) of row v (little-endian packing in uint32).
+ *   Wq      [V, D * bits / 32] uint32;  scales, biases [V, D / group_size] bf16.
+ *   bits    4 or 8;  group_size 32, 64 or 128 dividing D; else CCE_EINVAL.
+ * The library computes s * q + b in fp32 and rounds it to bf16 (nearest-even)
+ * one vocab chunk (16384 rows) at a time into the workspace; the chunk then
+ * takes the bf16 path of cce_forward / cce_backward, so every other argument,
+ * output and error behaves as there.  The results are those of cce_forward /
+ * cce_backward on the bf16-rounded dequantised head.
+ */
+
+/* Workspace bytes for cce_forward_q / cce_backward_q: cce_workspace_bytes plus
+ * one bf16 chunk of the dequantised head (16384 x D) and two [M] fp32 rows;
+ * independent of V above one chunk.  0 for invalid sizes.  Host-only. */
+size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D);
+
+/* Forward over the quantised head; outputs as for cce_forward.  The running
+ * (max, sum-exp) of each row is folded chunk by chunk in a fixed order. */
+cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales,
+                         const void* biases, int bits, int group_size,
+                         const int32_t* y, int64_t M, int64_t V, int64_t D, float softcap,
+                         float* logp, float* lse, uint32_t* dev_status,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Backward over the quantised head: dh [M, D] fp32 out (overwritten), as for
+ * cce_backward; no dW (the head is frozen). */
+cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
+                          const void* biases, int bits, int group_size,
+                          const int32_t* y, const float* lse, const float* coef,
+                          int64_t M, int64_t V, int64_t D, float softcap,
+                          float filter_eps, float block_eps, float* dh,
+                          uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,11 @@ SIGNATURES = {
                             _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "pref_epilogue": (_c_i, [_c_p, _c_p, _c_p, _c_i64, ctypes.c_int32, _c_i, _c_f, _c_f, _c_f, _c_f,
                              _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_workspace_bytes_q": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "cce_forward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_i64, _c_i64, _c_i64, _c_f,
+                             _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_backward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                              _c_i64, _c_f, _c_f, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
 }
 
 _lib = None
@@ -84,6 +89,10 @@ def workspace_bytes(M: int, V: int, D: int) -> int:
     return int(load().cce_workspace_bytes(int(M), int(V), int(D)))
 
 
+def workspace_bytes_q(M: int, V: int, D: int) -> int:
+    return int(load().cce_workspace_bytes_q(int(M), int(V), int(D)))
+
+
 def _check(fn: str, status: int):
     if status != CCE_OK:
         raise CCEError(fn, status)
@@ -119,10 +128,10 @@ class Head:
     and reused by every call; calls enqueue on the given (or current) stream.
     """
 
-    def __init__(self, M: int, V: int, D: int, device=None):
+    def __init__(self, M: int, V: int, D: int, device=None, quantized: bool = False):
         self.M, self.V, self.D = int(M), int(V), int(D)
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-        nbytes = workspace_bytes(self.M, self.V, self.D)
+        nbytes = (workspace_bytes_q if quantized else workspace_bytes)(self.M, self.V, self.D)
         if nbytes == 0:
             raise ValueError(f"invalid sizes M={M} V={V} D={D}")
         self.ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -207,6 +216,50 @@ class Head:
                                  self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
         _check("cce_backward", st)
         return dh, dW
+
+    # -- quantised (frozen) head ---------------------------------------------
+    def _quant_args(self, Wq, scales, biases, bits: int, group_size: int):
+        V, D = self.V, self.D
+        if bits not in (4, 8) or group_size not in (32, 64, 128) or D % group_size:
+            raise ValueError(f"unsupported quantisation bits={bits} group_size={group_size} D={D}")
+        if Wq.dtype == torch.uint32:
+            Wq = Wq.view(torch.int32)
+        return (_dev(Wq, "Wq", torch.int32, (V, D * bits // 32)),
+                _bf16(scales, "scales", (V, D // group_size)),
+                _bf16(biases, "biases", (V, D // group_size)), int(bits), int(group_size))
+
+    def forward_q(self, h, Wq, scales, biases, bits: int, group_size: int, y, logp=None, lse=None,
+                  stream=None, softcap: float = 0.0):
+        """Forward over an affine-quantised head (needs a Head built with quantized=True)."""
+        M, V, D = self.M, self.V, self.D
+        if logp is None:
+            logp = torch.empty(M, dtype=torch.float32, device=self.device)
+        if lse is None:
+            lse = torch.empty(M, dtype=torch.float32, device=self.device)
+        st = load().cce_forward_q(_bf16(h, "h", (M, D)), *self._quant_args(Wq, scales, biases, bits, group_size),
+                                  _dev(y, "y", torch.int32, (M,)), M, V, D, float(softcap),
+                                  _dev(logp, "logp", torch.float32, (M,)),
+                                  _dev(lse, "lse", torch.float32, (M,)),
+                                  self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
+        _check("cce_forward_q", st)
+        return logp, lse
+
+    def backward_q(self, h, Wq, scales, biases, bits: int, group_size: int, y, lse, coef,
+                   filter_eps: float = 0.0, block_eps: float = 0.0, dh=None, stream=None,
+                   softcap: float = 0.0):
+        """dh of an affine-quantised (frozen) head."""
+        M, V, D = self.M, self.V, self.D
+        if dh is None:
+            dh = torch.empty((M, D), dtype=torch.float32, device=self.device)
+        st = load().cce_backward_q(_bf16(h, "h", (M, D)), *self._quant_args(Wq, scales, biases, bits, group_size),
+                                   _dev(y, "y", torch.int32, (M,)),
+                                   _dev(lse, "lse", torch.float32, (M,)),
+                                   _dev(coef, "coef", torch.float32, (M,)), M, V, D,
+                                   float(softcap), float(filter_eps), float(block_eps),
+                                   _dev(dh, "dh", torch.float32, (M, D)),
+                                   self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
+        _check("cce_backward_q", st)
+        return dh
 
     def read_status(self) -> int:
         torch.cuda.synchronize(self.device)

@@ -29,15 +29,6 @@ bool sizes_ok(int64_t M, int64_t V, int64_t D) {
   return M >= 1 && V >= 1 && D >= 1 && M <= kMaxM && V <= kMaxV && D <= kMaxD;
 }
 
-// Forward vocab split: T tiles per workgroup so that nMt * S workgroups cover
-// the vocabulary in about one round of 256 workgroups (one per CU).
-void fwd_split(int64_t nMt, int64_t nVt, int& S, int& T) {
-  const int64_t tiles = nMt * nVt;
-  int64_t t = (tiles + 255) / 256;
-  if (t < 1) t = 1;
-  T = (int)t;
-  S = (int)((nVt + t - 1) / t);
-}
 // Upper bound of the partial slots over all V for this M (so the workspace does
 // not grow with V): the splits over the full vocab tiles plus one slot for a
 // ragged last tile.
@@ -46,6 +37,8 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
   size_t part_m, part_s, tgt, pairs, g, flags, total;
+  // quantised head only: running (max, sum-exp) and the bf16 chunk buffer
+  size_t run_m, run_s, wbuf, total_q;
 };
 
 Layout layout(int64_t M, int64_t V, int64_t D) {
@@ -68,6 +61,10 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   L.total = off;
+  L.run_m = take((size_t)L.Mpad * sizeof(float));
+  L.run_s = take((size_t)L.Mpad * sizeof(float));
+  L.wbuf = take((size_t)L.Vc * D * 2);
+  L.total_q = off;
   return L;
 }
 
@@ -97,7 +94,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int cce_abi_version(void) { return 3; }
+int cce_abi_version(void) { return 4; }
 
 const char* cce_status_string(int status) {
   switch (status) {
@@ -114,6 +111,11 @@ const char* cce_status_string(int status) {
 size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D) {
   if (!sizes_ok(M, V, D)) return 0;
   return layout(M, V, D).total;
+}
+
+size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D) {
+  if (!sizes_ok(M, V, D)) return 0;
+  return layout(M, V, D).total_q;
 }
 
 cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M, int64_t V,
@@ -137,7 +139,7 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
   a.nMt = (int)L.nMt;
   a.nVt = (int)((V + kTile - 1) / kTile);
   a.S = a.T = 0;
-  if (V / kTile > 0) fwd_split(a.nMt, V / kTile, a.S, a.T);  // over the full vocab tiles
+  if (V / kTile > 0) cce::fwd_split_tiles(a.nMt, (int)(V / kTile), a.S, a.T);  // full vocab tiles
   a.Mpad = (int)L.Mpad;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
   a.softcap = softcap;
@@ -244,6 +246,102 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
   a.flags = reinterpret_cast<int*>(base + L.flags);
   a.status = dev_status;
+  return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
+                                                                                : CCE_ELAUNCH;
+}
+
+static bool quant_ok(const void* Wq, const void* scales, const void* biases, int bits,
+                     int group_size, int64_t D) {
+  if (!Wq || !scales || !biases) return false;
+  if (bits != 4 && bits != 8) return false;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return false;
+  return D % group_size == 0;
+}
+
+cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales, const void* biases,
+                         int bits, int group_size, const int32_t* y, int64_t M, int64_t V,
+                         int64_t D, float softcap, float* logp, float* lse, uint32_t* dev_status,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !y || !logp || !lse || !dev_status || !ws) return CCE_EINVAL;
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
+  if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
+  if (!quant_ok(Wq, scales, biases, bits, group_size, D)) return CCE_EINVAL;
+  const Layout L = layout(M, V, D);
+  if (ws_bytes < L.total_q || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return CCE_EWORKSPACE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  char* base = static_cast<char*>(ws);
+  cce::FwdQArgs a{};
+  a.f.H = static_cast<const cce::u16*>(h);
+  a.f.W = nullptr;
+  a.f.y = y;
+  a.f.M = (int)M;
+  a.f.V = (int)V;
+  a.f.D = (int)D;
+  a.f.nMt = (int)L.nMt;
+  a.f.Mpad = (int)L.Mpad;
+  a.f.vec = (D % 8 == 0) && aligned16(h);  // the chunk buffer is aligned by construction
+  a.f.softcap = softcap;
+  a.f.part_m = reinterpret_cast<float*>(base + L.part_m);
+  a.f.part_s = reinterpret_cast<float*>(base + L.part_s);
+  a.f.tgt = reinterpret_cast<float*>(base + L.tgt);
+  a.f.logp = logp;
+  a.f.lse = lse;
+  a.f.status = dev_status;
+  a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
+                    static_cast<const cce::u16*>(biases), bits, group_size};
+  a.Vc = (int)L.Vc;
+  a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);
+  a.run_m = reinterpret_cast<float*>(base + L.run_m);
+  a.run_s = reinterpret_cast<float*>(base + L.run_s);
+  return cce::launch_forward_quant(a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? CCE_OK
+             : CCE_ELAUNCH;
+}
+
+cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
+                          const void* biases, int bits, int group_size, const int32_t* y,
+                          const float* lse, const float* coef, int64_t M, int64_t V, int64_t D,
+                          float softcap, float filter_eps, float block_eps, float* dh,
+                          uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  if (!h || !y || !lse || !coef || !dh || !dev_status || !ws) return CCE_EINVAL;
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
+  if (!(filter_eps >= 0.f) || !(block_eps >= 0.f) || !isfinite(filter_eps) || !isfinite(block_eps))
+    return CCE_EINVAL;
+  if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
+  if (!quant_ok(Wq, scales, biases, bits, group_size, D)) return CCE_EINVAL;
+  const Layout L = layout(M, V, D);
+  if (ws_bytes < L.total_q || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return CCE_EWORKSPACE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  char* base = static_cast<char*>(ws);
+  cce::BwdArgs a{};
+  a.H = static_cast<const cce::u16*>(h);
+  a.W = nullptr;
+  a.y = y;
+  a.lse = lse;
+  a.coef = coef;
+  a.M = (int)M;
+  a.V = (int)V;
+  a.D = (int)D;
+  a.nMt = (int)L.nMt;
+  a.Mpad = (int)L.Mpad;
+  a.Dpad = (int)L.Dpad;
+  a.Vc = (int)L.Vc;
+  a.vec = (D % 8 == 0) && aligned16(h);
+  a.softcap = softcap;
+  a.filter_eps = filter_eps;
+  a.block_eps = block_eps;
+  a.dh = dh;
+  a.dW = nullptr;
+  a.G = reinterpret_cast<cce::u16*>(base + L.g);
+  a.flags = reinterpret_cast<int*>(base + L.flags);
+  a.status = dev_status;
+  a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
+                    static_cast<const cce::u16*>(biases), bits, group_size};
+  a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
 }

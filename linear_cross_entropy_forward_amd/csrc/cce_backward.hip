@@ -220,7 +220,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
     const int vlen = a.V - v0 < a.Vc ? a.V - v0 : a.Vc;
     const int nvt = (vlen + kTile - 1) / kTile;
-    const u16* Wc = a.W + (size_t)v0 * a.D;
+    const u16* Wc = a.q.Wq ? nullptr : a.W + (size_t)v0 * a.D;
+    if (a.q.Wq) {  // quantised head: this chunk, dequantised into the chunk buffer
+      if ((e = launch_dequant(a.q, v0, vlen, a.D, a.Wbuf, st)) != hipSuccess) return e;
+      Wc = a.Wbuf;
+    }
     // 1. recompute + gradient tile
     {
       const int n = pad8(a.nMt * nvt);
@@ -255,9 +259,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
                   (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt,
                   pad8(a.nMt * nDt), a.flags, fstride, 1, v0 == 0 ? 0 : 1};
       GemmProb dw{OpRef{a.G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
-                  (size_t)kTile, a.Mpad, a.dW + (size_t)v0 * a.D, a.D, vlen, a.D, nvt, nDt,
+                  (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen, a.D, nvt, nDt,
                   pad8(nvt * nDt), a.flags, 1, fstride, 0};
-      const dim3 grid(dh.nl + dw.nl);
+      // the quantised head is frozen: dh only
+      const dim3 grid(a.q.Wq ? dh.nl : dh.nl + dw.nl);
       if (a.vec) {
         if (skip) hipLaunchKernelGGL((k_grads<true, true>), grid, dim3(NT), 0, st, dh, dw);
         else hipLaunchKernelGGL((k_grads<false, true>), grid, dim3(NT), 0, st, dh, dw);

@@ -200,9 +200,17 @@ static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int
 #undef CCE_FWD
 }
 
-hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
+void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {
+  const long long tiles = (long long)nMt * nVt;
+  long long t = (tiles + 255) / 256;
+  if (t < 1) t = 1;
+  T = (int)t;
+  S = (int)((nVt + t - 1) / t);
+}
+
+hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {
   const int full = a.V / TILE;  // full vocab tiles
-  int slots = 0;
+  slots = 0;
   if (full > 0) {
     launch_fwd_tiles<false>(a, a.S, a.T, 0, full, 0, st);
     slots = a.S;
@@ -211,14 +219,24 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
     launch_fwd_tiles<true>(a, 1, 1, full, full + 1, slots, st);
     slots += 1;
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_merge(const FwdArgs& a, const float* pm, const float* ps, int slots,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, pm, ps, a.tgt, a.y,
+                     a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
+  int slots = 0;
+  hipError_t e = launch_forward_tiles(a, slots, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_target_logit, dim3((a.M + 3) / 4), dim3(256), 0, st, a.H, a.W, a.y, a.M, a.V,
                      a.D, a.softcap, a.tgt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, a.part_m, a.part_s,
-                     a.tgt, a.y, a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status);
-  return hipGetLastError();
+  return launch_forward_merge(a, a.part_m, a.part_s, slots, st);
 }
 
 }  // namespace cce

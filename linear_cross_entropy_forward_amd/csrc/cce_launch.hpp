@@ -32,6 +32,41 @@ struct FwdArgs {
   unsigned* status;
 };
 hipError_t launch_forward(const FwdArgs& a, hipStream_t st);
+// Forward split: T vocab tiles per workgroup so that nMt * S workgroups cover
+// nVt tiles in about one round of 256 workgroups (one per CU).
+void fwd_split_tiles(int nMt, int nVt, int& S, int& T);
+// The forward's tile launches (full tiles, then a ragged last tile) writing
+// `slots` partial (max, sum-exp) slots, and the final merge of `slots` slots.
+hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st);
+hipError_t launch_forward_merge(const FwdArgs& a, const float* pm, const float* ps, int slots,
+                                hipStream_t st);
+
+// An affine-quantised head: per row v and group g of `group` columns a scale
+// and a bias (bf16), codes of `bits` bits packed little-endian in uint32 words
+// along the row; value s * q + b.
+struct QuantW {
+  const unsigned* Wq;
+  const u16* scale;
+  const u16* bias;
+  int bits, group;
+};
+
+// Forward over a quantised head: per vocab chunk of at most Vc rows, the chunk
+// is dequantised into Wbuf (bf16, [vlen, D]) and run through the forward
+// kernels; the chunk's partials fold into run_m / run_s ([Mpad] each).
+struct FwdQArgs {
+  FwdArgs f;  // f.W is unused; f.V is the whole vocabulary
+  QuantW q;
+  int Vc;
+  u16* Wbuf;
+  float* run_m;
+  float* run_s;
+};
+hipError_t launch_forward_quant(const FwdQArgs& a, hipStream_t st);
+
+// Dequantise rows v0 .. v0+vlen of a quantised head into dst ([vlen, D] bf16,
+// row-major): fp32 s * q + b, rounded to bf16 (round-to-nearest-even).
+hipError_t launch_dequant(const QuantW& q, int v0, int vlen, int D, u16* dst, hipStream_t st);
 
 struct EpiArgs {
   const float* logp;
@@ -67,6 +102,10 @@ struct BwdArgs {
   u16* G;      // [Mpad, Vc] bf16, blocked (256 x 32 blocks)
   int* flags;  // [nMt, Vc / kTile]
   unsigned* status;
+  // quantised head (q.Wq != null): each chunk is dequantised into Wbuf first,
+  // and dW is not formed (the quantised head is frozen; dW may be null)
+  QuantW q;
+  u16* Wbuf;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 

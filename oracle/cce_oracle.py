@@ -38,7 +38,11 @@ reason in the design notes of the repository):
     family with gamma replaced by beta * gamma); IPO is the reference-free
     (s)^2 on the length-normalised means; the hinge's derivative at its kink is
     taken as 0; every member may add the NLL term with a weight (0 for pure
-    SimPO, 1 for ORPO and the gamma-hybrid).
+    SimPO, 1 for ORPO and the gamma-hybrid);
+  * the quantised head's value is s * q + b exactly, and its contractions take
+    that value rounded to bf16 (the pages dequantise into fp32 on their GPU;
+    bf16 is the operand type of the matrix cores used here), so the quantised
+    forward and backward are the bf16 head's on round_bf16(dequantize(...)).
 
 Every function here has a pin in the test-suite (closed forms, library special
 cases, finite differences, brute force, invariants); none is "parity unpinned"
@@ -105,6 +109,17 @@ def dequantize(Wq: np.ndarray, scale: np.ndarray, bias: np.ndarray, bits: int,
         q[:, j::per] = ((Wq >> np.uint64(bits * j)) & mask).astype(np.float64)
     g = np.arange(D) // group_size
     return np.asarray(scale, np.float64)[:, g] * q + np.asarray(bias, np.float64)[:, g]
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Each value rounded to the nearest bfloat16 number (8 significant bits,
+    ties to the even significand), returned as fp64.  The operand precision of
+    the quantised head's contractions: its dequantised values are taken in
+    bf16, like the bf16 head's.  Normal range only (no subnormal or overflow
+    handling: head values are far from both ends)."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)               # x = m * 2^e with 0.5 <= |m| < 1 (m = 0 for x = 0)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # np.round: half to even
 
 
 def logsumexp_rows(Z: np.ndarray) -> np.ndarray:

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == {"cce_abi_version", "cce_status_string", "cce_workspace_bytes", "cce_forward",
-                     "orpo_epilogue", "pref_epilogue", "cce_backward"}
+                     "orpo_epilogue", "pref_epilogue", "cce_backward", "cce_workspace_bytes_q",
+                     "cce_forward_q", "cce_backward_q"}
     assert names == set(B.SIGNATURES)
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert B.load().cce_abi_version() == 3
+    assert B.load().cce_abi_version() == 4
 
 
 def test_status_strings():
@@ -146,6 +147,51 @@ def test_backward_argument_errors():
     assert lib.cce_backward(*a) == B.CCE_EWORKSPACE
 
 
+def test_quant_workspace_adds_one_chunk_buffer():
+    M, D = 8192, 2560
+    sizes = [B.workspace_bytes_q(M, V, D) for V in (32768, 262144, 1 << 20)]
+    assert len(set(sizes)) == 1
+    extra = sizes[0] - B.workspace_bytes(M, 262144, D)
+    # the bf16 chunk of the dequantised head (16384 x D) and two fp32 rows of Mpad
+    assert 2 * 16384 * D + 8 * M <= extra < 2 * 16384 * D + 8 * M + 3 * 256
+    assert B.workspace_bytes_q(0, 10, 64) == 0
+
+
+def test_forward_q_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes_q(300, 1000, 128)
+    # h, Wq, scales, biases, bits, group_size, y, M, V, D, softcap, logp, lse, dev_status, ws,
+    # ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, 4, 64, FAKE, 300, 1000, 128, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws,
+          None]
+    for i, bad in ((0, None), (1, None), (2, None), (3, None), (6, None), (11, None), (13, None),
+                   (4, 2), (4, 16), (5, 16), (5, 256), (10, float("nan")), (10, -1.0)):
+        a = list(ok); a[i] = bad
+        assert lib.cce_forward_q(*a) == B.CCE_EINVAL, (i, bad)
+    a = list(ok); a[9] = 96                       # D not a multiple of the group
+    assert lib.cce_forward_q(*a) == B.CCE_EINVAL
+    a = list(ok); a[7] = 0
+    assert lib.cce_forward_q(*a) == B.CCE_ESHAPE
+    a = list(ok); a[15] = B.workspace_bytes(300, 1000, 128)    # the bf16 workspace is too small
+    assert lib.cce_forward_q(*a) == B.CCE_EWORKSPACE
+
+
+def test_backward_q_argument_errors():
+    lib = B.load()
+    ws = B.workspace_bytes_q(300, 1000, 128)
+    # h, Wq, scales, biases, bits, group_size, y, lse, coef, M, V, D, softcap, filter_eps,
+    # block_eps, dh, dev_status, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, FAKE, 300, 1000, 128, 0.0, 0.0, 0.0, FAKE, FAKE,
+          FAKE * 256, ws, None]
+    for i, bad in ((1, None), (8, None), (15, None), (4, 3), (5, 48), (13, -1.0), (14, float("inf"))):
+        a = list(ok); a[i] = bad
+        assert lib.cce_backward_q(*a) == B.CCE_EINVAL, (i, bad)
+    a = list(ok); a[10] = -1
+    assert lib.cce_backward_q(*a) == B.CCE_ESHAPE
+    a = list(ok); a[18] = ws - 1
+    assert lib.cce_backward_q(*a) == B.CCE_EWORKSPACE
+
+
 def test_valid_call_without_gfx950_is_refused():
     """With valid arguments and no gfx950 device the library refuses (it never
     falls back to another path)."""
@@ -158,4 +204,8 @@ def test_valid_call_without_gfx950_is_refused():
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
     st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    assert st == B.CCE_EDEVICE
+    wq = B.workspace_bytes_q(300, 1000, 64)
+    st = lib.cce_forward_q(FAKE, FAKE, FAKE, FAKE, 4, 32, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE,
+                           FAKE * 256, wq, None)
     assert st == B.CCE_EDEVICE

@@ -748,3 +748,31 @@ def test_p12_dequantize_round_trip(bits, group):
     codes = np.rint((Wd - b[:, g]) / step)
     assert codes.min() >= 0 and codes.max() <= levels
     assert np.allclose(codes, (Wd - b[:, g]) / step, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------
+# P13: bf16 rounding of the dequantised head (the quantised path's operands)
+# ----------------------------------------------------------------------------
+def test_p13_round_bf16_hand_values():
+    """Ties go to the even significand; anything past a tie goes up; the bf16
+    grid (8 significant bits) is fixed."""
+    u = 2.0 ** -7                                    # one bf16 ulp at 1
+    vals = np.array([1.0, 1 + u / 2, 1 + 1.5 * u, 1 + u / 2 + 2.0 ** -30, 1 + u / 2 - 2.0 ** -30,
+                     -(1 + 1.5 * u), 3.0 * 2.0 ** -140 * 2 ** 20, 0.0, 255.0, 257.0, 259.0])
+    want = [1.0, 1.0, 1 + 2 * u, 1 + u, 1.0, -(1 + 2 * u), 3.0 * 2.0 ** -120, 0.0, 255.0, 256.0,
+            260.0]
+    assert O.round_bf16(vals).tolist() == want
+
+
+def test_p13_round_bf16_matches_torch_on_fp32_values():
+    """On values exactly representable in fp32 the rounding equals torch's own
+    fp32 -> bfloat16 conversion (round to nearest even), a library routine."""
+    import torch
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    # plant exact ties: the low 16 bits 0x8000 with even and odd kept parts
+    xi = x.view(np.uint32).copy()
+    xi[:2000] = (xi[:2000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = xi.view(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
