@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="final-logit softcap c (logits c*tanh(z/c)); 0 = off (the metric's config)")
+    ap.add_argument("--quant", type=int, default=0, choices=(0, 4, 8),
+                    help="affine-quantised frozen head with 4- or 8-bit codes (forward + dh); "
+                         "0 = the bf16 head (the metric's config)")
+    ap.add_argument("--group", type=int, default=64, help="quantisation group size (with --quant)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
     ap.add_argument("--v-sweep", action="store_true",
                     help="time one step and record workspace / peak device memory at "
@@ -197,9 +201,20 @@ def main():
     feps = wl.filter_eps if args.filter_eps is None else args.filter_eps
     print(f"[bench] workload {wl.name} M={wl.M} V={wl.V} D={wl.D} filter_eps={feps}",
           file=sys.stderr, flush=True)
-    head = B.Head(wl.M, wl.V, wl.D, dev)
+    quant = args.quant != 0
+    head = B.Head(wl.M, wl.V, wl.D, dev, quantized=quant)
     h = B.to_device_bits(wl.h_bits, dev)
-    W = B.to_device_bits(wl.W_bits, dev)
+    if quant:
+        print(f"[bench] quantising the head to {args.quant}-bit codes, group {args.group} (host)",
+              file=sys.stderr, flush=True)
+        qh = WL.quantize_affine(WL.bf16_bits_to_f32(wl.W_bits), args.quant, args.group)
+        Wq = torch.from_numpy(qh.Wq.view(np.int32)).to(dev)
+        Ws = B.to_device_bits(qh.scale_bits, dev)
+        Wb = B.to_device_bits(qh.bias_bits, dev)
+        del qh
+        W = None
+    else:
+        W = B.to_device_bits(wl.W_bits, dev)
     y = torch.from_numpy(wl.y).to(dev)
     seg = torch.from_numpy(wl.seg).to(dev)
     logp = torch.empty(wl.M, dtype=torch.float32, device=dev)
@@ -208,19 +223,28 @@ def main():
     out5 = torch.empty(5, dtype=torch.float32, device=dev)
     pst = torch.empty((wl.n_pairs, 8), dtype=torch.float32, device=dev)
     dh = torch.empty((wl.M, wl.D), dtype=torch.float32, device=dev)
-    dW = torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
+    dW = None if quant else torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def one_step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        head.forward(h, W, y, logp, lse, stream=stream, softcap=args.softcap)
+        if quant:
+            head.forward_q(h, Wq, Ws, Wb, args.quant, args.group, y, logp, lse, stream=stream,
+                           softcap=args.softcap)
+        else:
+            head.forward(h, W, y, logp, lse, stream=stream, softcap=args.softcap)
         if ev is not None:
             ev[1].record(stream)
         head.epilogue(logp, y, seg, wl.n_pairs, wl.lam, wl.scope, out5, pst, coef, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        head.backward(h, W, y, lse, coef, feps, feps, dh, dW, stream=stream, softcap=args.softcap)
+        if quant:
+            head.backward_q(h, Wq, Ws, Wb, args.quant, args.group, y, lse, coef, feps, feps, dh,
+                            stream=stream, softcap=args.softcap)
+        else:
+            head.backward(h, W, y, lse, coef, feps, feps, dh, dW, stream=stream,
+                          softcap=args.softcap)
         if ev is not None:
             ev[3].record(stream)
 
@@ -249,14 +273,17 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f}, epi {epi_ms:.3f}, "
           f"bwd {bwd_ms:.3f}); wall {wall:.2f} s", file=sys.stderr, flush=True)
 
-    flops = 8.0 * wl.M * wl.V * wl.D
+    # contractions per step: forward logits, recomputed logits, dh, and dW (bf16 head
+    # only: the quantised head is frozen)
+    n_contr = 3 if quant else 4
+    flops = 2.0 * n_contr * wl.M * wl.V * wl.D
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens_s = wl.M / (ms_step * 1e-3)
     # the longest single launch, timed live: the forward GEMM + online-LSE kernel
     # (cce_forward = k_fwd + target-logit and merge kernels of a few microseconds)
     fwd_flops = 2.0 * wl.M * wl.V * wl.D
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
-    bwd_tflops = 3.0 * fwd_flops / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = (n_contr - 1) * fwd_flops / (bwd_ms * 1e-3) / 1e12
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
         try:
@@ -267,8 +294,13 @@ def main():
         except Exception:
             traffic = None
 
+    metric = "fused CCE fwd+bwd tokens/s and % bf16 MFMA peak (8*M*V*D FLOPs)"
+    workload = wl.name
+    if quant:
+        metric = "fused CCE fwd+bwd(dh) tokens/s over a quantised frozen head (6*M*V*D FLOPs)"
+        workload = f"{wl.name}_q{args.quant}g{args.group}"
     result = {
-        "metric": "fused CCE fwd+bwd tokens/s and % bf16 MFMA peak (8*M*V*D FLOPs)",
+        "metric": metric,
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -280,22 +312,26 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) hidden, N(0,0.02^2) head, Zipf(1.1) targets)",
-        "config": {"workload": wl.name, "M": wl.M, "V": wl.V, "D": wl.D, "n_pairs": wl.n_pairs,
+        "config": {"workload": workload, "M": wl.M, "V": wl.V, "D": wl.D, "n_pairs": wl.n_pairs,
                    "lambda": wl.lam, "scope": "full" if wl.scope == 0 else "response",
-                   "filter_eps": feps, "softcap": args.softcap, "parallelism": "none (1 GPU)"},
+                   "filter_eps": feps, "softcap": args.softcap,
+                   "quant": {"bits": args.quant, "group": args.group} if quant else None,
+                   "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "phase_ms": {"forward": round(fwd_ms, 4), "epilogue": round(epi_ms, 4),
                      "backward": round(bwd_ms, 4)},
-        "workspace_bytes": B.workspace_bytes(wl.M, wl.V, wl.D),
+        "workspace_bytes": (B.workspace_bytes_q if quant else B.workspace_bytes)(wl.M, wl.V, wl.D),
         "device_status": status,
-        "roofline": {"kernel": "k_fwd (cce_forward)", "bound": "mfma",
+        "roofline": {"kernel": "cce_forward_q (k_dequant + k_fwd per chunk)" if quant
+                     else "k_fwd (cce_forward)", "bound": "mfma",
                      "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": None if quant else traffic},
         # the backward's kernels (per vocab chunk: recompute, then dh + dW) timed
         # together live around cce_backward: 3 contractions of 2*M*V*D FLOPs
-        "roofline_backward": {"kernels": "k_recompute + k_grads (cce_backward)",
+        "roofline_backward": {"kernels": "k_dequant + k_recompute + k_grads (dh) (cce_backward_q)"
+                              if quant else "k_recompute + k_grads (cce_backward)",
                               "bound": "mfma", "achieved": round(bwd_tflops, 2),
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
@@ -309,7 +345,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not quant:
         print(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
     else:
