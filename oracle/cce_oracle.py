@@ -418,16 +418,67 @@ def grad_logits(Z: np.ndarray, lse: np.ndarray, y: np.ndarray, coef: np.ndarray,
     return coef[:, None] * (P - onehot) * dcapped(Z, softcap)
 
 
+# ----------------------------------------------------------------------------
+# Block skip ([P1] §5.1 "Apple-CCE backward skips": the blockMax skip, whose
+# per-(row, vocab block) maximum the forward saves next to the LSE).  The
+# vocabulary and the rows are cut into blocks of `block` (256 here, from 0);
+# block_max[b, i] is the largest (capped) logit of row i over vocab block b.
+# A (row block, vocab block) pair is dead when every softmax entry in it,
+# exp(block_max - lse) bounding them all, is below block_eps and none of its
+# rows has its target in the vocab block; dead pairs contribute nothing.
+# ----------------------------------------------------------------------------
+def block_max(H: np.ndarray, W: np.ndarray, softcap: float = 0.0, block: int = 256) -> np.ndarray:
+    """[ceil(V / block), M]: the largest capped logit of each row per vocab block."""
+    H = np.asarray(H, np.float64)
+    W = np.asarray(W, np.float64)
+    M, V = H.shape[0], W.shape[0]
+    nb = (V + block - 1) // block
+    out = np.empty((nb, M), np.float64)
+    step = _row_chunk(V)
+    for i0 in range(0, M, step):
+        i1 = min(M, i0 + step)
+        Z = capped(logits(H[i0:i1], W), softcap)
+        for b in range(nb):
+            out[b, i0:i1] = Z[:, b * block:(b + 1) * block].max(axis=1)
+    return out
+
+
+def dead_blocks(bmax: np.ndarray, lse: np.ndarray, y: np.ndarray, block_eps: float,
+                block: int = 256) -> np.ndarray:
+    """[ceil(M / block), ceil(V / block)] bool: the pairs the block skip drops."""
+    bmax = np.asarray(bmax, np.float64)
+    lse = np.asarray(lse, np.float64)
+    y = np.asarray(y, np.int64)
+    nvb, M = bmax.shape
+    nrb = (M + block - 1) // block
+    dead = np.zeros((nrb, nvb), bool)
+    if block_eps <= 0.0:
+        return dead
+    pmax = np.exp(bmax - lse[None, :])                    # [nvb, M]
+    for a in range(nrb):
+        rows = slice(a * block, min(M, (a + 1) * block))
+        below = pmax[:, rows].max(axis=1) < block_eps
+        has_tgt = np.zeros(nvb, bool)
+        yt = y[rows]
+        has_tgt[np.unique(yt[yt >= 0] // block)] = True
+        dead[a] = below & ~has_tgt
+    return dead
+
+
 def backward(H: np.ndarray, W: np.ndarray, y: np.ndarray, lse: np.ndarray, coef: np.ndarray,
-             filter_eps: float = 0.0, softcap: float = 0.0):
+             filter_eps: float = 0.0, softcap: float = 0.0, block_eps: float = 0.0,
+             block: int = 256):
     """Returns (dh[M,D], dW[V,D]) in fp64, given the forward's lse and the
-    epilogue's coef."""
+    epilogue's coef; block_eps > 0 applies the block skip."""
     H = np.asarray(H, np.float64)
     W = np.asarray(W, np.float64)
     y = np.asarray(y, np.int64)
     lse = np.asarray(lse, np.float64)
     coef = np.asarray(coef, np.float64)
     M, V = H.shape[0], W.shape[0]
+    dead = None
+    if block_eps > 0.0:
+        dead = dead_blocks(block_max(H, W, softcap, block), lse, y, block_eps, block)
     dh = np.zeros_like(H)
     dW = np.zeros_like(W)
     step = _row_chunk(V)
@@ -435,6 +486,9 @@ def backward(H: np.ndarray, W: np.ndarray, y: np.ndarray, lse: np.ndarray, coef:
         i1 = min(M, i0 + step)
         G = grad_logits(logits(H[i0:i1], W), lse[i0:i1], y[i0:i1], coef[i0:i1], filter_eps,
                         softcap)
+        if dead is not None:
+            G = np.where(dead[np.arange(i0, i1)[:, None] // block, np.arange(V)[None, :] // block],
+                         0.0, G)
         dh[i0:i1] = G @ W
         dW += G.T @ H[i0:i1]
     return dh, dW

@@ -776,3 +776,83 @@ def test_p13_round_bf16_matches_torch_on_fp32_values():
     x = xi.view(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+# ----------------------------------------------------------------------------
+# P14: the forward-saved block maximum and the block skip ([P1] §5.1 backward
+# skips)
+# ----------------------------------------------------------------------------
+def test_p14_block_max_brute_force():
+    rng = np.random.default_rng(14)
+    M, V, D, blk = 7, 23, 5, 4
+    H, W = rng.standard_normal((M, D)), rng.standard_normal((V, D))
+    for cap in (0.0, 1.5):
+        got = O.block_max(H, W, cap, block=blk)
+        assert got.shape == (6, M)
+        for b in range(6):
+            for i in range(M):
+                best = -math.inf
+                for v in range(b * blk, min(V, (b + 1) * blk)):
+                    z = sum(H[i, d] * W[v, d] for d in range(D))
+                    if cap:
+                        z = cap * math.tanh(z / cap)
+                    best = max(best, z)
+                assert got[b, i] == pytest.approx(best, rel=1e-12, abs=1e-12)
+
+
+def test_p14_block_max_bounds_the_lse():
+    """max over blocks of block_max is the row max, so it is <= lse <= that + log V."""
+    rng = np.random.default_rng(15)
+    H, W = rng.standard_normal((40, 16)), rng.standard_normal((1000, 16))
+    y = rng.integers(0, 1000, 40)
+    _, lse = O.forward(H, W, y)
+    top = O.block_max(H, W).max(axis=0)
+    assert np.allclose(top, O.logits(H, W).max(axis=1), rtol=0, atol=1e-12)
+    assert np.all(top <= lse + 1e-12) and np.all(lse <= top + math.log(1000) + 1e-12)
+
+
+def test_p14_block_skip_equals_filter_when_eps_match():
+    """Every entry of a dead block is below eps and not a target, so with
+    block_eps = filter_eps the skip removes nothing the filter keeps."""
+    rng = np.random.default_rng(16)
+    M, V, D, blk = 20, 64, 6, 8
+    H = rng.standard_normal((M, D))
+    H[:, 0] = 3.0
+    W = rng.standard_normal((V, D)) * 0.5
+    W[16:40, 0] = -5.0                        # vocab blocks 2..4 far down for every row
+    y = rng.integers(0, 16, M)
+    coef = rng.standard_normal(M)
+    _, lse = O.forward(H, W, y)
+    eps = 1e-3
+    dead = O.dead_blocks(O.block_max(H, W, block=blk), lse, y, eps, block=blk)
+    assert dead.any() and not dead.all()
+    a = O.backward(H, W, y, lse, coef, filter_eps=eps, block_eps=eps, block=blk)
+    b = O.backward(H, W, y, lse, coef, filter_eps=eps)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_p14_block_skip_zeroes_exactly_the_dead_blocks():
+    """Without the filter, the skip removes exactly the dead blocks' terms:
+    dW rows of a vocab block dead for every row block are 0, and the dh
+    difference equals the dead entries' contribution computed directly."""
+    rng = np.random.default_rng(17)
+    M, V, D, blk = 16, 32, 4, 8
+    H = np.abs(rng.standard_normal((M, D))) + 1.0
+    W = rng.standard_normal((V, D)) * 0.1
+    W[8:16] = -4.0                             # vocab block 1 far below for every row
+    y = rng.integers(16, 32, M)
+    coef = rng.standard_normal(M)
+    _, lse = O.forward(H, W, y)
+    dead = O.dead_blocks(O.block_max(H, W, block=blk), lse, y, 1e-4, block=blk)
+    assert dead[:, 1].all() and not dead[:, [0, 2, 3]].any()
+    dh_s, dW_s = O.backward(H, W, y, lse, coef, block_eps=1e-4, block=blk)
+    dh, dW = O.backward(H, W, y, lse, coef)
+    assert np.all(dW_s[8:16] == 0.0)
+    assert np.array_equal(dW_s[:8], dW[:8]) and np.array_equal(dW_s[16:], dW[16:])
+    P = np.exp(O.logits(H, W[8:16]) - lse[:, None])
+    assert np.allclose(dh - dh_s, (coef[:, None] * P) @ W[8:16], rtol=1e-10, atol=1e-14)
+    # target inside the block keeps it alive for that row block
+    y2 = y.copy()
+    y2[3] = 9
+    dead2 = O.dead_blocks(O.block_max(H, W, block=blk), lse, y2, 1e-4, block=blk)
+    assert not dead2[0, 1] and dead2[1, 1]
