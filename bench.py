@@ -39,6 +39,9 @@ def parse():
                     help="affine-quantised frozen head with 4- or 8-bit codes (forward + dh); "
                          "0 = the bf16 head (the metric's config)")
     ap.add_argument("--group", type=int, default=64, help="quantisation group size (with --quant)")
+    ap.add_argument("--block-max", action="store_true",
+                    help="the forward saves the per-(vocab block, row) maximum and the backward "
+                         "decides its block skip from it before recomputing a tile")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
     ap.add_argument("--v-sweep", action="store_true",
                     help="time one step and record workspace / peak device memory at "
@@ -224,6 +227,8 @@ def main():
     pst = torch.empty((wl.n_pairs, 8), dtype=torch.float32, device=dev)
     dh = torch.empty((wl.M, wl.D), dtype=torch.float32, device=dev)
     dW = None if quant else torch.empty((wl.V, wl.D), dtype=torch.float32, device=dev)
+    bmax = (torch.empty(B.block_max_shape(wl.M, wl.V), dtype=torch.float32, device=dev)
+            if args.block_max else None)
     stream = torch.cuda.current_stream()
 
     def one_step(ev=None):
@@ -231,9 +236,9 @@ def main():
             ev[0].record(stream)
         if quant:
             head.forward_q(h, Wq, Ws, Wb, args.quant, args.group, y, logp, lse, stream=stream,
-                           softcap=args.softcap)
+                           softcap=args.softcap, block_max=bmax)
         else:
-            head.forward(h, W, y, logp, lse, stream=stream, softcap=args.softcap)
+            head.forward(h, W, y, logp, lse, stream=stream, softcap=args.softcap, block_max=bmax)
         if ev is not None:
             ev[1].record(stream)
         head.epilogue(logp, y, seg, wl.n_pairs, wl.lam, wl.scope, out5, pst, coef, stream=stream)
@@ -241,10 +246,10 @@ def main():
             ev[2].record(stream)
         if quant:
             head.backward_q(h, Wq, Ws, Wb, args.quant, args.group, y, lse, coef, feps, feps, dh,
-                            stream=stream, softcap=args.softcap)
+                            stream=stream, softcap=args.softcap, block_max=bmax)
         else:
             head.backward(h, W, y, lse, coef, feps, feps, dh, dW, stream=stream,
-                          softcap=args.softcap)
+                          softcap=args.softcap, block_max=bmax)
         if ev is not None:
             ev[3].record(stream)
 
@@ -311,11 +316,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) hidden, N(0,0.02^2) head, Zipf(1.1) targets)",
+        "data": "synthetic (seeded N(0,1) hidden, N(0,0.02^2) head, Zipf(1.1) targets"
+                + (", token-frequency prior -1.1 ln(1+v) on the logits)" if wl.name == "gemma4b_peaked"
+                   else ")"),
         "config": {"workload": workload, "M": wl.M, "V": wl.V, "D": wl.D, "n_pairs": wl.n_pairs,
                    "lambda": wl.lam, "scope": "full" if wl.scope == 0 else "response",
                    "filter_eps": feps, "softcap": args.softcap,
                    "quant": {"bits": args.quant, "group": args.group} if quant else None,
+                   "block_max": bool(args.block_max),
                    "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -92,13 +92,18 @@ size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D);
  *            CCE_EINVAL.
  *   logp     [M] fp32 out: z_{i,y_i} - lse_i, and 0 for rows with y_i = -1
  *   lse      [M] fp32 out: logsumexp_v z_{i,v} (written for every row)
+ *   block_max  NULL, or [ceil(V / 256), M] fp32 out: the largest (capped)
+ *            logit of row i over vocab block b = [256 b, 256 b + 256), at
+ *            block_max[b * M + i] ("Training — design …" §5.1: the blockMax
+ *            the forward saves for the backward's block skip).  Costs one
+ *            barrier per tile and 4 bytes per row per vocab block.
  *   dev_status  uint32 (device) OR-ed with CCE_DERR_TARGET / _NONFINITE
  *   ws, ws_bytes  device workspace of at least cce_workspace_bytes(M, V, D)
  *                 bytes, 256-byte aligned; contents on entry are ignored.
  */
 cce_status cce_forward(const void* h, const void* W, const int32_t* y,
                        int64_t M, int64_t V, int64_t D, float softcap,
-                       float* logp, float* lse, uint32_t* dev_status,
+                       float* logp, float* lse, float* block_max, uint32_t* dev_status,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -172,12 +177,18 @@ cce_status pref_epilogue(const float* logp, const int32_t* y, const int32_t* seg
  *   block_eps   >= 0; a 256x256 (row, vocab) tile whose largest softmax entry
  *               is below it and that holds no row's target is skipped.
  *               0 and 0 give the exact gradient.
+ *   block_max   NULL, or the forward's block_max (same h, W, softcap): with
+ *               block_eps > 0 the skip test is taken from it before the tile's
+ *               logits are recomputed, so a skipped tile costs no contraction
+ *               at all (without it the test needs the recomputed tile; the
+ *               decision is the same up to fp32 rounding).  Ignored when
+ *               block_eps = 0.
  *   dh [M, D] fp32 out (overwritten); dW [V, D] fp32 out (overwritten).
  *   G is rounded to bf16 (round-to-nearest-even) before the two contractions;
  *   accumulation is fp32.
  */
 cce_status cce_backward(const void* h, const void* W, const int32_t* y,
-                        const float* lse, const float* coef,
+                        const float* lse, const float* coef, const float* block_max,
                         int64_t M, int64_t V, int64_t D, float softcap,
                         float filter_eps, float block_eps,
                         float* dh, float* dW, uint32_t* dev_status,
@@ -212,7 +223,7 @@ size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D);
 cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales,
                          const void* biases, int bits, int group_size,
                          const int32_t* y, int64_t M, int64_t V, int64_t D, float softcap,
-                         float* logp, float* lse, uint32_t* dev_status,
+                         float* logp, float* lse, float* block_max, uint32_t* dev_status,
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Backward over the quantised head: dh [M, D] fp32 out (overwritten), as for
@@ -220,7 +231,7 @@ cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales,
 cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
                           const void* biases, int bits, int group_size,
                           const int32_t* y, const float* lse, const float* coef,
-                          int64_t M, int64_t V, int64_t D, float softcap,
+                          const float* block_max, int64_t M, int64_t V, int64_t D, float softcap,
                           float filter_eps, float block_eps, float* dh,
                           uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
 

@@ -28,19 +28,19 @@ SIGNATURES = {
     "cce_abi_version": (ctypes.c_int, []),
     "cce_status_string": (ctypes.c_char_p, [_c_i]),
     "cce_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
-    "cce_forward": (_c_i, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz,
-                           _c_p]),
+    "cce_forward": (_c_i, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p, _c_p, _c_p,
+                           _c_sz, _c_p]),
     "orpo_epilogue": (_c_i, [_c_p, _c_p, _c_p, _c_i64, ctypes.c_int32, _c_f, _c_i, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_sz, _c_p]),
-    "cce_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_f, _c_f,
-                            _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_f,
+                            _c_f, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "pref_epilogue": (_c_i, [_c_p, _c_p, _c_p, _c_i64, ctypes.c_int32, _c_i, _c_f, _c_f, _c_f, _c_f,
                              _c_i, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "cce_workspace_bytes_q": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
     "cce_forward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_i64, _c_i64, _c_i64, _c_f,
-                             _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
-    "cce_backward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_i64, _c_i64,
-                              _c_i64, _c_f, _c_f, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+                             _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_backward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                              _c_i64, _c_i64, _c_f, _c_f, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
 }
 
 _lib = None
@@ -93,6 +93,16 @@ def workspace_bytes_q(M: int, V: int, D: int) -> int:
     return int(load().cce_workspace_bytes_q(int(M), int(V), int(D)))
 
 
+def block_max_shape(M: int, V: int) -> Tuple[int, int]:
+    """Shape of the forward's saved block maximum: [ceil(V / 256), M]."""
+    return ((int(V) + 255) // 256, int(M))
+
+
+def _opt(t, name: str, shape) -> int:
+    """Pointer of an optional fp32 device tensor (None -> NULL)."""
+    return 0 if t is None else _dev(t, name, torch.float32, shape)
+
+
 def _check(fn: str, status: int):
     if status != CCE_OK:
         raise CCEError(fn, status)
@@ -141,7 +151,10 @@ class Head:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     # -- forward --------------------------------------------------------------
-    def forward(self, h, W, y, logp=None, lse=None, stream=None, softcap: float = 0.0):
+    def forward(self, h, W, y, logp=None, lse=None, stream=None, softcap: float = 0.0,
+                block_max=None):
+        """block_max: None, or an fp32 [ceil(V / 256), M] tensor that receives the
+        per-(vocab block, row) maximum logit for the backward's block skip."""
         M, V, D = self.M, self.V, self.D
         if logp is None:
             logp = torch.empty(M, dtype=torch.float32, device=self.device)
@@ -151,6 +164,7 @@ class Head:
                                 _dev(y, "y", torch.int32, (M,)), M, V, D, float(softcap),
                                 _dev(logp, "logp", torch.float32, (M,)),
                                 _dev(lse, "lse", torch.float32, (M,)),
+                                _opt(block_max, "block_max", block_max_shape(M, V)),
                                 self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
         _check("cce_forward", st)
         return logp, lse
@@ -200,7 +214,7 @@ class Head:
 
     # -- backward -------------------------------------------------------------
     def backward(self, h, W, y, lse, coef, filter_eps: float = 0.0, block_eps: float = 0.0,
-                 dh=None, dW=None, stream=None, softcap: float = 0.0):
+                 dh=None, dW=None, stream=None, softcap: float = 0.0, block_max=None):
         M, V, D = self.M, self.V, self.D
         if dh is None:
             dh = torch.empty((M, D), dtype=torch.float32, device=self.device)
@@ -209,7 +223,8 @@ class Head:
         st = load().cce_backward(_bf16(h, "h", (M, D)), _bf16(W, "W", (V, D)),
                                  _dev(y, "y", torch.int32, (M,)),
                                  _dev(lse, "lse", torch.float32, (M,)),
-                                 _dev(coef, "coef", torch.float32, (M,)), M, V, D,
+                                 _dev(coef, "coef", torch.float32, (M,)),
+                                 _opt(block_max, "block_max", block_max_shape(M, V)), M, V, D,
                                  float(softcap), float(filter_eps), float(block_eps),
                                  _dev(dh, "dh", torch.float32, (M, D)),
                                  _dev(dW, "dW", torch.float32, (V, D)),
@@ -229,7 +244,7 @@ class Head:
                 _bf16(biases, "biases", (V, D // group_size)), int(bits), int(group_size))
 
     def forward_q(self, h, Wq, scales, biases, bits: int, group_size: int, y, logp=None, lse=None,
-                  stream=None, softcap: float = 0.0):
+                  stream=None, softcap: float = 0.0, block_max=None):
         """Forward over an affine-quantised head (needs a Head built with quantized=True)."""
         M, V, D = self.M, self.V, self.D
         if logp is None:
@@ -240,13 +255,14 @@ class Head:
                                   _dev(y, "y", torch.int32, (M,)), M, V, D, float(softcap),
                                   _dev(logp, "logp", torch.float32, (M,)),
                                   _dev(lse, "lse", torch.float32, (M,)),
+                                  _opt(block_max, "block_max", block_max_shape(M, V)),
                                   self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
         _check("cce_forward_q", st)
         return logp, lse
 
     def backward_q(self, h, Wq, scales, biases, bits: int, group_size: int, y, lse, coef,
                    filter_eps: float = 0.0, block_eps: float = 0.0, dh=None, stream=None,
-                   softcap: float = 0.0):
+                   softcap: float = 0.0, block_max=None):
         """dh of an affine-quantised (frozen) head."""
         M, V, D = self.M, self.V, self.D
         if dh is None:
@@ -254,7 +270,8 @@ class Head:
         st = load().cce_backward_q(_bf16(h, "h", (M, D)), *self._quant_args(Wq, scales, biases, bits, group_size),
                                    _dev(y, "y", torch.int32, (M,)),
                                    _dev(lse, "lse", torch.float32, (M,)),
-                                   _dev(coef, "coef", torch.float32, (M,)), M, V, D,
+                                   _dev(coef, "coef", torch.float32, (M,)),
+                                   _opt(block_max, "block_max", block_max_shape(M, V)), M, V, D,
                                    float(softcap), float(filter_eps), float(block_eps),
                                    _dev(dh, "dh", torch.float32, (M, D)),
                                    self.status.data_ptr(), self.ws_ptr, self.ws_bytes, _stream_ptr(stream))
@@ -277,9 +294,12 @@ def to_device_bits(bits, device) -> torch.Tensor:
 
 
 def step(head: Head, h, W, y, seg, n_pairs, lam, scope, filter_eps=0.0, block_eps=0.0, stream=None,
-         softcap=0.0):
-    """One whole pass: forward, epilogue, backward (all enqueued on one stream)."""
-    logp, lse = head.forward(h, W, y, stream=stream, softcap=softcap)
+         softcap=0.0, block_max=None):
+    """One whole pass: forward, epilogue, backward (all enqueued on one stream).
+    block_max: None, or a [ceil(V / 256), M] fp32 tensor the forward fills and
+    the backward's block skip reads."""
+    logp, lse = head.forward(h, W, y, stream=stream, softcap=softcap, block_max=block_max)
     out5, pstats, coef = head.epilogue(logp, y, seg, n_pairs, lam, scope, stream=stream)
-    dh, dW = head.backward(h, W, y, lse, coef, filter_eps, block_eps, stream=stream, softcap=softcap)
+    dh, dW = head.backward(h, W, y, lse, coef, filter_eps, block_eps, stream=stream, softcap=softcap,
+                           block_max=block_max)
     return dict(logp=logp, lse=lse, out5=out5, pair_stats=pstats, coef=coef, dh=dh, dW=dW)

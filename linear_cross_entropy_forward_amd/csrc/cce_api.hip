@@ -94,7 +94,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int cce_abi_version(void) { return 4; }
+int cce_abi_version(void) { return 5; }
 
 const char* cce_status_string(int status) {
   switch (status) {
@@ -119,8 +119,8 @@ size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D) {
 }
 
 cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M, int64_t V,
-                       int64_t D, float softcap, float* logp, float* lse, uint32_t* dev_status,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       int64_t D, float softcap, float* logp, float* lse, float* block_max,
+                       uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!h || !W || !y || !logp || !lse || !dev_status || !ws) return CCE_EINVAL;
   if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
@@ -149,6 +149,7 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
   a.logp = logp;
   a.lse = lse;
   a.status = dev_status;
+  a.bm = block_max;
   return cce::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                : CCE_ELAUNCH;
 }
@@ -211,7 +212,8 @@ cce_status pref_epilogue(const float* logp, const int32_t* y, const int32_t* seg
 }
 
 cce_status cce_backward(const void* h, const void* W, const int32_t* y, const float* lse,
-                        const float* coef, int64_t M, int64_t V, int64_t D, float softcap,
+                        const float* coef, const float* block_max, int64_t M, int64_t V,
+                        int64_t D, float softcap,
                         float filter_eps, float block_eps, float* dh, float* dW,
                         uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!h || !W || !y || !lse || !coef || !dh || !dW || !dev_status || !ws) return CCE_EINVAL;
@@ -246,6 +248,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
   a.flags = reinterpret_cast<int*>(base + L.flags);
   a.status = dev_status;
+  a.bm = block_max;
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
 }
@@ -260,8 +263,8 @@ static bool quant_ok(const void* Wq, const void* scales, const void* biases, int
 
 cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales, const void* biases,
                          int bits, int group_size, const int32_t* y, int64_t M, int64_t V,
-                         int64_t D, float softcap, float* logp, float* lse, uint32_t* dev_status,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         int64_t D, float softcap, float* logp, float* lse, float* block_max,
+                         uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!h || !y || !logp || !lse || !dev_status || !ws) return CCE_EINVAL;
   if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
   if (!sizes_ok(M, V, D)) return CCE_ESHAPE;
@@ -289,6 +292,7 @@ cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales, 
   a.f.logp = logp;
   a.f.lse = lse;
   a.f.status = dev_status;
+  a.f.bm = block_max;
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
   a.Vc = (int)L.Vc;
@@ -302,8 +306,9 @@ cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales, 
 
 cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
                           const void* biases, int bits, int group_size, const int32_t* y,
-                          const float* lse, const float* coef, int64_t M, int64_t V, int64_t D,
-                          float softcap, float filter_eps, float block_eps, float* dh,
+                          const float* lse, const float* coef, const float* block_max, int64_t M,
+                          int64_t V, int64_t D, float softcap, float filter_eps, float block_eps,
+                          float* dh,
                           uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
   if (!h || !y || !lse || !coef || !dh || !dev_status || !ws) return CCE_EINVAL;
   if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
@@ -339,6 +344,7 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
   a.flags = reinterpret_cast<int*>(base + L.flags);
   a.status = dev_status;
+  a.bm = block_max;
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
   a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);

@@ -37,18 +37,39 @@ namespace cce {
 // softmax entry is exp(c t - lse) and the chain rule through the cap adds the
 // factor 1 - t^2 (sech^2(z / c)).  The tile-skip test uses the per-token
 // largest t, which gives the largest softmax entry of that token.
+//
+// bm (the forward's saved block maximum of this chunk, tile vt of token j at
+// bm[vt * M + j]; null when not given or block_eps = 0): the tile-skip test is
+// taken before the recompute, from exp(bm - lse) and the targets, and a
+// skipped tile is not recomputed at all.
 template <bool VEC, bool FILTER, bool KTAIL, bool CAP>
 __global__ __launch_bounds__(NT, 1) void k_recompute(
     const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
     const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
     int vlen, int nMt, int nvt, float softcap, float filter_eps, float block_eps,
-    u16* __restrict__ G, int* __restrict__ flags, int nkbV) {
+    u16* __restrict__ G, int* __restrict__ flags, int nkbV, const float* __restrict__ bm) {
   __shared__ Smem sm;
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   int mt, vt;
   if (!map_tile(blockIdx.x, gridDim.x, nMt, nvt, 8, mt, vt)) return;
+  int* flag = flags + (size_t)mt * (nkbV / 8) + vt;
+  if (bm) {
+    // one token per thread: is any softmax entry of the tile >= block_eps, or
+    // is the token's target among the tile's vocab rows?
+    const int j = mt * TILE + tid;
+    int keep = 0;
+    if (j < M) {
+      const float pm = fast_exp2((bm[(size_t)vt * M + j] - lse[j]) * LOG2E);
+      const int o = y[j] - (v0 + vt * TILE);
+      keep = (pm >= block_eps || (unsigned)o < (unsigned)TILE) ? 1 : 0;
+    }
+    if (!__syncthreads_or(keep)) {
+      if (tid == 0) *flag = 0;
+      return;
+    }
+  }
 
   floatx16 acc[4][4];
   gemm_tile<VEC, false, KTAIL>(OpRef{Wc + (size_t)vt * TILE * D, D, min(TILE, vlen - vt * TILE), D},
@@ -63,7 +84,7 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
   for (int jj = 0; jj < 4; ++jj) {
     const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
     const bool ok = j < M;
-    nlse[jj] = ok ? -lse[j] * LOG2E : 0.f;
+    nlse[jj] = ok ? -lse[j] * LOG2E : NEG_INF;  // padding rows: no softmax entries
     cf[jj] = ok ? coef[j] : 0.f;
     const int yy = ok ? y[j] : -1;
     off[jj] = (yy >= 0) ? yy - (v0 + vl0) - 4 * half : -1000000;
@@ -100,8 +121,7 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) pmax = fmaxf(pmax, fast_exp2(fmaf(tmax[jj], c1, nlse[jj])));
   }
-  int* flag = flags + (size_t)mt * (nkbV / 8) + vt;
-  if (block_eps > 0.f) {
+  if (block_eps > 0.f && !bm) {
     // skip the tile if every softmax entry is below block_eps and no token of
     // the tile has its target among the tile's vocab rows
     const bool keep_lane = pmax >= block_eps || any_tgt_lane;
@@ -220,6 +240,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
     const int vlen = a.V - v0 < a.Vc ? a.V - v0 : a.Vc;
     const int nvt = (vlen + kTile - 1) / kTile;
+    const float* bmc = (a.bm && a.block_eps > 0.f) ? a.bm + (size_t)(v0 / kTile) * a.M : nullptr;
     const u16* Wc = a.q.Wq ? nullptr : a.W + (size_t)v0 * a.D;
     if (a.q.Wq) {  // quantised head: this chunk, dequantised into the chunk buffer
       if ((e = launch_dequant(a.q, v0, vlen, a.D, a.Wbuf, st)) != hipSuccess) return e;
@@ -231,7 +252,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
 #define CCE_RECOMPUTE(VEC, FILT, KT, CAP)                                                          \
   hipLaunchKernelGGL((k_recompute<VEC, FILT, KT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y,    \
                      a.lse, a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, a.softcap, a.filter_eps,       \
-                     a.block_eps, a.G, a.flags, nkbV)
+                     a.block_eps, a.G, a.flags, nkbV, bmc)
 #define CCE_RECOMPUTE_F(VEC, KT, CAP)                                                              \
   do {                                                                                             \
     if (filt) CCE_RECOMPUTE(VEC, true, KT, CAP); else CCE_RECOMPUTE(VEC, false, KT, CAP);          \

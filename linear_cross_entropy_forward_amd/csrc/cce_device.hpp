@@ -501,12 +501,72 @@ __device__ __forceinline__ void gemm_step(const DmaOperand<AMODE, KTAIL>& da,
 // ring_lds), unrolled by 4 so that every access names its stage statically
 // (constant LDS offsets).  The order between the direct-to-LDS loads and the
 // reads of their data is kept by the explicit vmcnt waits and barriers only.
-// SKIP: a slice whose 256-wide K block is flagged inactive streams through
-// the ring without its MFMAs.  A tile with every block active takes the
-// regular loop; otherwise a variant that branches around each sub-step's 16
-// MFMAs as a whole (no interleaving, no unrolling): control flow between
-// interleaved MFMAs leaves the register allocator unable to keep the
-// accumulators in place.
+// SKIP (K a multiple of 256): 256-wide K blocks flagged inactive take no
+// part.  A tile with every block active takes the regular loop.  With at most
+// 64 blocks the active ones form a 64-bit mask and the same pipelined loop
+// walks only their slices (a scalar cursor yields the K offset of the slice
+// three steps ahead), so an inactive block costs neither loads nor MFMAs.
+// With more blocks, a variant streams every slice through the ring and
+// branches around each sub-step's 16 MFMAs as a whole (no interleaving, no
+// unrolling): control flow between interleaved MFMAs leaves the register
+// allocator unable to keep the accumulators in place.
+struct SliceCursor {
+  unsigned long long m;  // active blocks not yet left behind (current one lowest)
+  int cb, cs;            // current block, slice within it
+  __device__ __forceinline__ void init(unsigned long long mask) {
+    m = mask;
+    cb = __builtin_ctzll(mask);
+    cs = 0;
+  }
+  // K offset of the cursor's slice, then advance; past the last active slice
+  // it keeps yielding in-range offsets of the last block (stages never read)
+  __device__ __forceinline__ int next() {
+    const int k = cb * TILE + cs * BK;
+    if (++cs == TILE / BK) {
+      cs = 0;
+      m &= m - 1ull;
+      if (m != 0ull) cb = __builtin_ctzll(m);
+    }
+    return k;
+  }
+};
+
+// The regular loop over the slices of the active blocks in `mask` only.
+template <int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
+__device__ __forceinline__ void gemm_loop_compact(const DmaOperand<AMODE, KTAIL>& da,
+                                                  const DmaOperand<BMODE, KTAIL>& db,
+                                                  const FragAddr<AK, BKM>& fa,
+                                                  unsigned long long mask,
+                                                  const unsigned char* ring, unsigned ring_lds,
+                                                  floatx16 (&acc)[4][4]) {
+  const int nsl = __builtin_popcountll(mask) * (TILE / BK);
+  if (nsl == 0) {  // nothing active: acc stays 0, no load was issued
+    __syncthreads();
+    return;
+  }
+  SliceCursor cur;
+  cur.init(mask);
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int k = cur.next();
+    da.issue_all(k, ring_lds + s * STAGE_BYTES);
+    db.issue_all(k, ring_lds + s * STAGE_BYTES + HALF_BYTES);
+  }
+  CCE_WAIT_VMCNT(16);  // slice 0 landed (slices 1 and 2 may be in flight)
+  ring_barrier();
+  Frags f0, f1;
+  load_frags(ring, fa, 0, f0);
+  for (int kt0 = 0; kt0 < nsl; kt0 += NSTAGE) {
+#pragma unroll
+    for (int j = 0; j < NSTAGE; ++j)
+      gemm_step(da, db, fa, cur.next(), ring + j * STAGE_BYTES,
+                ring + ((j + 1) & 3) * STAGE_BYTES, ring_lds + ((j + 3) & 3) * STAGE_BYTES, f0, f1,
+                acc);
+  }
+  CCE_WAIT_VMCNT(0);
+  __syncthreads();
+}
+
 template <bool SKIP, int AMODE, int BMODE, bool KTAIL, bool AK, bool BKM>
 __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
                                           const DmaOperand<BMODE, KTAIL>& db,
@@ -519,10 +579,19 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
     // one pass over the tile's K-block flags (lanes stride over the blocks),
     // before any direct-to-LDS load is in flight
     const int nkb = (nk * BK + TILE - 1) / TILE;
-    bool lane_ok = true;
-    for (int kb = (int)(threadIdx.x & 63); kb < nkb; kb += 64)
-      lane_ok &= kflags[(size_t)kb * kflag_stride] != 0;
-    all_active = __ballot(!lane_ok) == 0ull;
+    const int lane = (int)(threadIdx.x & 63);
+    if (nkb <= 64) {
+      const bool on = lane < nkb && kflags[(size_t)lane * kflag_stride] != 0;
+      const unsigned long long mask = __ballot(on);
+      if (__builtin_popcountll(mask) != nkb) {
+        gemm_loop_compact(da, db, fa, mask, ring, ring_lds, acc);
+        return;
+      }
+    } else {
+      bool lane_ok = true;
+      for (int kb = lane; kb < nkb; kb += 64) lane_ok &= kflags[(size_t)kb * kflag_stride] != 0;
+      all_active = __ballot(!lane_ok) == 0ull;
+    }
   }
   const int klast = (nk - 1) * BK;
 #pragma unroll
@@ -571,8 +640,8 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
 
 // acc = A[0:256, 0:K] . B[0:256, 0:K]^T for the operand tiles A and B, each in
 // the form AMODE / BMODE (KTAIL: a row-form operand may end inside a K-slice).
-// SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive; its
-// MFMAs are skipped (its slices still stream through LDS).
+// SKIP: kflags[kb * kflag_stride] == 0 marks 256-wide K block kb inactive (K
+// a multiple of 256); it takes no part (see gemm_loop).
 // VEC: the pipelined loop above (slice kt sits in stage kt % 4; slices past
 // the last one are clamped to it, their stages no longer read); it ends by
 // draining every load and a barrier, so LDS is free.  Otherwise one slice at

@@ -18,16 +18,24 @@
 // target logit is one dot product per row, computed by its own small kernel.
 // The merge kernel combines the partials of a row in a fixed order: results
 // are deterministic and nothing depends on atomics.
+//
+// Saved block maximum ([P1] §5.1, the blockMax the backward's block skip
+// reads): optionally every tile also writes, per token, the largest (capped)
+// logit over its 256 vocab rows, bm[tile][token]; the two waves that share a
+// token combine through a small double-buffered LDS array, one barrier per
+// tile.
 #include "cce_device.hpp"
 #include "cce_launch.hpp"
 
 namespace cce {
 
-// Online-softmax update of one vocab tile for the 4 tokens this lane owns.
-// TAIL: the tile runs past V; entries with v >= V take no part.
+// Online-softmax update of one vocab tile for the 4 tokens this lane owns;
+// tmx gets the lane's largest entry per token.  TAIL: the tile runs past V;
+// entries with v >= V take no part.
 template <bool TAIL>
 __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int vw, int V, int half,
-                                                float (&m_run)[4], float (&s_run)[4]) {
+                                                float (&m_run)[4], float (&s_run)[4],
+                                                float (&tmx)[4]) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float mx = NEG_INF;
@@ -38,6 +46,7 @@ __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int
         const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
         if (ok) mx = fmaxf(mx, acc[ii][jj][r]);
       }
+    tmx[jj] = mx;
     const float mn = fmaxf(m_run[jj], mx);
     if (TAIL && mn == NEG_INF) continue;  // no valid entry yet for this lane
     const float nb = -mn * LOG2E;
@@ -56,14 +65,17 @@ __device__ __forceinline__ void fwd_tile_update(const floatx16 (&acc)[4][4], int
 
 // Workgroup (mt, split) runs vocab tiles [t0 + split*T, min(t0 + (split+1)*T, t1))
 // and writes partial slot slot0 + split.  CAP: every logit is replaced by
-// softcap * tanh(z / softcap) before the online update.
-template <bool VEC, bool KTAIL, bool TAIL, bool CAP>
+// softcap * tanh(z / softcap) before the online update.  BM: tile t's per-token
+// maximum goes to bm[t * M + token].
+template <bool VEC, bool KTAIL, bool TAIL, bool CAP, bool BM>
 __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const u16* __restrict__ W,
                                                int M, int V, int D, int nMt, int S, int T, int t0,
                                                int t1, int slot0, int nlaunch, float softcap,
                                                float* __restrict__ part_m,
-                                               float* __restrict__ part_s, int Mpad) {
+                                               float* __restrict__ part_s, int Mpad,
+                                               float* __restrict__ bm) {
   __shared__ Smem sm;
+  __shared__ float bmx[2][TILE];
   int mt, split;
   if (!map_tile(blockIdx.x, nlaunch, nMt, S, 8, mt, split)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -93,7 +105,26 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[ii][jj][r] = softcap * tanh_scaled(acc[ii][jj][r], k2);
     }
-    fwd_tile_update<TAIL>(acc, v0 + wi * 128, V, half, m_run, s_run);
+    float tmx[4];
+    fwd_tile_update<TAIL>(acc, v0 + wi * 128, V, half, m_run, s_run, tmx);
+    if (BM) {
+      // lanes l and l^32 hold the same token, waves wi = 0 and 1 too
+      float* xb = bmx[t & 1];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) tmx[jj] = fmaxf(tmx[jj], __shfl_xor(tmx[jj], 32));
+      if (wi == 1 && half == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) xb[wj * 128 + jj * 32 + lane] = tmx[jj];
+      }
+      __syncthreads();
+      if (wi == 0 && half == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = mt * TILE + wj * 128 + jj * 32 + lane;
+          if (j < M) bm[(size_t)t * M + j] = fmaxf(tmx[jj], xb[wj * 128 + jj * 32 + lane]);
+        }
+      }
+    }
   }
 
   // lanes l and l^32 hold the same token: merge them
@@ -186,9 +217,14 @@ static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int
                              hipStream_t st) {
   const int n = a.nMt * S;
   const int nl = (n + 7) / 8 * 8;
+#define CCE_FWD2(VEC, KT, CAP, BM)                                                              \
+  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL, CAP, BM>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M,  \
+                     a.V, a.D, a.nMt, S, T, t0, t1, slot0, nl, a.softcap, a.part_m, a.part_s,     \
+                     a.Mpad, a.bm)
 #define CCE_FWD(VEC, KT, CAP)                                                                   \
-  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL, CAP>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, \
-                     a.D, a.nMt, S, T, t0, t1, slot0, nl, a.softcap, a.part_m, a.part_s, a.Mpad)
+  do {                                                                                          \
+    if (a.bm) CCE_FWD2(VEC, KT, CAP, true); else CCE_FWD2(VEC, KT, CAP, false);                \
+  } while (0)
   const bool cap = a.softcap > 0.f;
   if (!a.vec) {
     if (cap) CCE_FWD(false, false, true); else CCE_FWD(false, false, false);
@@ -198,6 +234,7 @@ static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int
     if (cap) CCE_FWD(true, false, true); else CCE_FWD(true, false, false);
   }
 #undef CCE_FWD
+#undef CCE_FWD2
 }
 
 void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {

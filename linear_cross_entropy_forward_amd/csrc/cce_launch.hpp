@@ -30,6 +30,9 @@ struct FwdArgs {
   float* logp;
   float* lse;
   unsigned* status;
+  // null, or the saved block maximum of this launch's vocab range: vocab tile t
+  // (relative to W) of token j at bm[t * M + j]
+  float* bm;
 };
 hipError_t launch_forward(const FwdArgs& a, hipStream_t st);
 // Forward split: T vocab tiles per workgroup so that nMt * S workgroups cover
@@ -106,6 +109,9 @@ struct BwdArgs {
   // and dW is not formed (the quantised head is frozen; dW may be null)
   QuantW q;
   u16* Wbuf;
+  // null, or the forward's saved block maximum ([ceil(V / 256), M]): with
+  // block_eps > 0 a tile's skip is decided from it before its recompute
+  const float* bm;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 

@@ -125,6 +125,7 @@ hipError_t launch_forward_quant(const FwdQArgs& a, hipStream_t st) {
     FwdArgs c = f;
     c.W = a.Wbuf;
     c.V = vlen;
+    c.bm = f.bm ? f.bm + (size_t)(v0 / kTile) * f.M : nullptr;
     c.nVt = (vlen + kTile - 1) / kTile;
     c.S = c.T = 0;
     if (vlen / kTile > 0) fwd_split_tiles(c.nMt, vlen / kTile, c.S, c.T);

@@ -19,7 +19,13 @@ here; these draws stand in for them):
     softmax), head weight ~ N(0, 0.02^2);
   * fp32 values are rounded to bf16 with round-to-nearest-even, once;
   * targets are Zipf(s=1.1) over the vocab, P(id=k) ~ (k+1)^-1.1 on [0, V),
-    drawn by inverse CDF (rank = id), or uniform for the tiny case.
+    drawn by inverse CDF (rank = id), or uniform for the tiny case;
+  * the "peaked" Gemma case adds a token-frequency prior to the logits, the
+    way a trained head concentrates the softmax on frequent ids: hidden
+    coordinate 0 is 1 on every row and head coordinate 0 of vocab row v is
+    -1.1 * ln(1 + v) (the targets' own Zipf exponent), so a logit is the
+    random part plus -1.1 ln(1 + v) and the rare-id vocab tiles carry almost
+    no softmax mass (what the backward's block skip exploits on real data).
 """
 from __future__ import annotations
 
@@ -164,11 +170,12 @@ class Workload:
         return 8.0 * self.M * self.V * self.D
 
 
-CONFIG_NAMES = ["tiny", "small_1b", "long_1b", "gemma4b_head", "stress"]
+CONFIG_NAMES = ["tiny", "small_1b", "long_1b", "gemma4b_head", "stress", "gemma4b_peaked"]
+PRIOR_EXPONENT = 1.1
 
 
 def _draw(k: int, M: int, D: int, V: int, spans, hidden_scale: float, targets: str,
-          keep_raw: bool, seed_k: Optional[int] = None):
+          keep_raw: bool, seed_k: Optional[int] = None, prior: bool = False):
     ss = np.random.SeedSequence(BASE_SEED + (k if seed_k is None else seed_k))
     s_h, s_w, s_y, _s_layout = ss.spawn(4)
     rh, rw, ry = (np.random.Generator(np.random.PCG64(s)) for s in (s_h, s_w, s_y))
@@ -176,6 +183,9 @@ def _draw(k: int, M: int, D: int, V: int, spans, hidden_scale: float, targets: s
     if hidden_scale != 1.0:
         h *= np.float32(hidden_scale)
     W = _normal_f32(rw, (V, D), 0.02)
+    if prior:
+        h[:, 0] = 1.0
+        W[:, 0] = (-PRIOR_EXPONENT * np.log1p(np.arange(V, dtype=np.float64))).astype(np.float32)
     seg = layout_pairs(spans)
     assert seg.shape[0] == M, (seg.shape, M)
     if targets == "zipf":
@@ -189,7 +199,8 @@ def _draw(k: int, M: int, D: int, V: int, spans, hidden_scale: float, targets: s
 
 def make_workload(name: str, V: Optional[int] = None, M_scale: float = 1.0,
                   seed_k: Optional[int] = None) -> Workload:
-    """Build one of the five named workloads.
+    """Build one of the named workloads (the five configurations, and the
+    Gemma-4B head with the token-frequency prior, "gemma4b_peaked").
 
     V overrides the vocab (used for the workspace-vs-V sweep and for reduced
     parity cases); M_scale shrinks every span (reduced parity cases).
@@ -211,6 +222,10 @@ def make_workload(name: str, V: Optional[int] = None, M_scale: float = 1.0,
     elif name == "gemma4b_head":
         spans = [(sc(2048, 0), sc(3072), sc(3072))]
         D, VV, hs, tg, lam, scope, feps = 2560, 262144, 1.0, "zipf", 0.1, SCOPE_FULL, 0.0
+    elif name == "gemma4b_peaked":
+        # the Gemma-4B head's shape and layout; the pages' default skip eps 1e-5
+        spans = [(sc(2048, 0), sc(3072), sc(3072))]
+        D, VV, hs, tg, lam, scope, feps = 2560, 262144, 1.0, "zipf", 0.1, SCOPE_FULL, 1e-5
     elif name == "stress":
         ss = np.random.SeedSequence(BASE_SEED + (k if seed_k is None else seed_k))
         r_layout = np.random.Generator(np.random.PCG64(ss.spawn(4)[3]))
@@ -224,7 +239,7 @@ def make_workload(name: str, V: Optional[int] = None, M_scale: float = 1.0,
         VV = int(V)
     M = int(sum(sum(sp) for sp in spans))
     hb, wb, y, seg, hr, wr = _draw(k, M, D, VV, spans, hs, tg, keep_raw=(name == "tiny"),
-                                   seed_k=seed_k)
+                                   seed_k=seed_k, prior=(name == "gemma4b_peaked"))
     return Workload(name=name, M=M, D=D, V=VV, h_bits=hb, W_bits=wb, y=y, seg=seg,
                     n_pairs=len(spans), lam=lam, scope=scope, filter_eps=feps,
                     h_f32_raw=hr, W_f32_raw=wr)

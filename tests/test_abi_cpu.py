@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert B.load().cce_abi_version() == 4
+    assert B.load().cce_abi_version() == 5
 
 
 def test_status_strings():
@@ -72,9 +72,9 @@ FAKE = 1 << 20   # a non-null pointer value; never dereferenced on these paths
 def test_forward_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    # h, W, y, M, V, D, softcap, logp, lse, dev_status, ws, ws_bytes, stream
-    ok = (FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
-    for i in (0, 1, 2, 7, 8, 9, 10):
+    # h, W, y, M, V, D, softcap, logp, lse, block_max, dev_status, ws, ws_bytes, stream
+    ok = (FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, None, FAKE, FAKE * 256, ws, None)
+    for i in (0, 1, 2, 7, 8, 10, 11):
         args = list(ok)
         args[i] = None
         assert lib.cce_forward(*args) == B.CCE_EINVAL
@@ -87,10 +87,10 @@ def test_forward_argument_errors():
         args[i] = 0
         assert lib.cce_forward(*args) == B.CCE_ESHAPE
     args = list(ok)
-    args[11] = ws - 1
+    args[12] = ws - 1
     assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
     args = list(ok)
-    args[10] = FAKE * 256 + 16          # misaligned workspace
+    args[11] = FAKE * 256 + 16          # misaligned workspace
     assert lib.cce_forward(*args) == B.CCE_EWORKSPACE
 
 
@@ -132,18 +132,18 @@ def test_pref_epilogue_argument_errors():
 def test_backward_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    # h, W, y, lse, coef, M, V, D, softcap, filter_eps, block_eps, dh, dW, dev_status, ws,
-    # ws_bytes, stream
-    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, 0.0, 0.0, FAKE, FAKE, FAKE, FAKE * 256,
-          ws, None]
-    for i, bad in ((8, -1.0), (8, float("nan")), (9, -1.0), (10, float("inf"))):
+    # h, W, y, lse, coef, block_max, M, V, D, softcap, filter_eps, block_eps, dh, dW, dev_status,
+    # ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 300, 1000, 64, 0.0, 0.0, 0.0, FAKE, FAKE, FAKE,
+          FAKE * 256, ws, None]
+    for i, bad in ((9, -1.0), (9, float("nan")), (10, -1.0), (11, float("inf"))):
         a = list(ok); a[i] = bad
         assert lib.cce_backward(*a) == B.CCE_EINVAL
-    a = list(ok); a[12] = None
+    a = list(ok); a[13] = None
     assert lib.cce_backward(*a) == B.CCE_EINVAL
-    a = list(ok); a[7] = -3
+    a = list(ok); a[8] = -3
     assert lib.cce_backward(*a) == B.CCE_ESHAPE
-    a = list(ok); a[15] = 1
+    a = list(ok); a[16] = 1
     assert lib.cce_backward(*a) == B.CCE_EWORKSPACE
 
 
@@ -160,11 +160,11 @@ def test_quant_workspace_adds_one_chunk_buffer():
 def test_forward_q_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes_q(300, 1000, 128)
-    # h, Wq, scales, biases, bits, group_size, y, M, V, D, softcap, logp, lse, dev_status, ws,
-    # ws_bytes, stream
-    ok = [FAKE, FAKE, FAKE, FAKE, 4, 64, FAKE, 300, 1000, 128, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws,
-          None]
-    for i, bad in ((0, None), (1, None), (2, None), (3, None), (6, None), (11, None), (13, None),
+    # h, Wq, scales, biases, bits, group_size, y, M, V, D, softcap, logp, lse, block_max,
+    # dev_status, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, 4, 64, FAKE, 300, 1000, 128, 0.0, FAKE, FAKE, None, FAKE,
+          FAKE * 256, ws, None]
+    for i, bad in ((0, None), (1, None), (2, None), (3, None), (6, None), (11, None), (14, None),
                    (4, 2), (4, 16), (5, 16), (5, 256), (10, float("nan")), (10, -1.0)):
         a = list(ok); a[i] = bad
         assert lib.cce_forward_q(*a) == B.CCE_EINVAL, (i, bad)
@@ -172,23 +172,23 @@ def test_forward_q_argument_errors():
     assert lib.cce_forward_q(*a) == B.CCE_EINVAL
     a = list(ok); a[7] = 0
     assert lib.cce_forward_q(*a) == B.CCE_ESHAPE
-    a = list(ok); a[15] = B.workspace_bytes(300, 1000, 128)    # the bf16 workspace is too small
+    a = list(ok); a[16] = B.workspace_bytes(300, 1000, 128)    # the bf16 workspace is too small
     assert lib.cce_forward_q(*a) == B.CCE_EWORKSPACE
 
 
 def test_backward_q_argument_errors():
     lib = B.load()
     ws = B.workspace_bytes_q(300, 1000, 128)
-    # h, Wq, scales, biases, bits, group_size, y, lse, coef, M, V, D, softcap, filter_eps,
-    # block_eps, dh, dev_status, ws, ws_bytes, stream
-    ok = [FAKE, FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, FAKE, 300, 1000, 128, 0.0, 0.0, 0.0, FAKE, FAKE,
-          FAKE * 256, ws, None]
-    for i, bad in ((1, None), (8, None), (15, None), (4, 3), (5, 48), (13, -1.0), (14, float("inf"))):
+    # h, Wq, scales, biases, bits, group_size, y, lse, coef, block_max, M, V, D, softcap,
+    # filter_eps, block_eps, dh, dev_status, ws, ws_bytes, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, 8, 32, FAKE, FAKE, FAKE, None, 300, 1000, 128, 0.0, 0.0, 0.0, FAKE,
+          FAKE, FAKE * 256, ws, None]
+    for i, bad in ((1, None), (8, None), (16, None), (4, 3), (5, 48), (14, -1.0), (15, float("inf"))):
         a = list(ok); a[i] = bad
         assert lib.cce_backward_q(*a) == B.CCE_EINVAL, (i, bad)
-    a = list(ok); a[10] = -1
+    a = list(ok); a[11] = -1
     assert lib.cce_backward_q(*a) == B.CCE_ESHAPE
-    a = list(ok); a[18] = ws - 1
+    a = list(ok); a[19] = ws - 1
     assert lib.cce_backward_q(*a) == B.CCE_EWORKSPACE
 
 
@@ -203,9 +203,10 @@ def test_valid_call_without_gfx950_is_refused():
         pass
     lib = B.load()
     ws = B.workspace_bytes(300, 1000, 64)
-    st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE, FAKE * 256, ws, None)
+    st = lib.cce_forward(FAKE, FAKE, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, None, FAKE, FAKE * 256, ws,
+                         None)
     assert st == B.CCE_EDEVICE
     wq = B.workspace_bytes_q(300, 1000, 64)
-    st = lib.cce_forward_q(FAKE, FAKE, FAKE, FAKE, 4, 32, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, FAKE,
-                           FAKE * 256, wq, None)
+    st = lib.cce_forward_q(FAKE, FAKE, FAKE, FAKE, 4, 32, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, None,
+                           FAKE, FAKE * 256, wq, None)
     assert st == B.CCE_EDEVICE
