@@ -21,6 +21,13 @@
 // ((t / 256) * (Vc / 32) + v / 32) * 8192 + (t % 256) * 32 + v % 32, so every
 // 256 x 32 slice dh streams is one contiguous 16 KB block, and every 32 x 256
 // slice dW streams is eight contiguous 2 KB pieces.
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
+#include <vector>
+
 #include "cce_device.hpp"
 #include "cce_launch.hpp"
 
@@ -174,6 +181,12 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
 // over an nA x nB tile grid launched as nl workgroups.  a / b describe tile 0;
 // tile ta of A starts a_tile elements after a.p, tile tb of B b_tile elements
 // after b.p (with b.cols reduced by tb*256).
+//
+// Split K (first problem only, the dh form: A blocked, B read transposed):
+// with ks > 1 every output tile is ks tasks, part q taking K blocks
+// [q*nb/ks, (q+1)*nb/ks) of the nb = K/256; part 0 writes C as above, part q > 0
+// writes (no accumulation) the partial tile P + (q-1)*p_part (leading dimension
+// ldc), and a later reduction adds the partials to C in the order q = 1, 2, ...
 struct GemmProb {
   OpRef a, b;
   size_t a_tile, b_tile;
@@ -184,6 +197,9 @@ struct GemmProb {
   const int* kflags;  // per 256-wide K block of A tile ta: kflags[ta*fa + kb*fk]
   int fa, fk;
   int accum;  // 1: C += result, 0: C = result
+  int ks;     // K parts (1: no split)
+  float* P;
+  size_t p_part;
 };
 
 // The dh and dW contractions of one vocab chunk in a single launch: workgroups
@@ -200,25 +216,33 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
   const GemmProb p = second ? p1 : p0;
   if (second) b -= p0.nl;
   int ta, tb;
-  if (!map_tile(b, p.nl, p.nA, p.nB, 8, ta, tb)) return;
+  if (!map_tile(b, p.nl, p.nA, p.nB * p.ks, 8, ta, tb)) return;
+  const int part = tb / p.nB;  // K part (0 unless the problem is split)
+  tb -= part * p.nB;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
-  const OpRef a{p.a.p + ta * p.a_tile, p.a.ld, p.a.rows, p.a.cols};
-  const OpRef bo{p.b.p + tb * p.b_tile, p.b.ld, p.b.rows, p.b.cols - tb * TILE};
-  const int* kf = SKIP ? p.kflags + (size_t)ta * p.fa : nullptr;
+  const int nb = p.K / TILE;
+  const int kb0 = part * nb / p.ks, kb1 = (part + 1) * nb / p.ks;
+  // part offsets (the split problem is of the dh form: A blocked, 8 blocks of
+  // 8192 elements per 256 K; B [k][i] with pitch ld)
+  const OpRef a{p.a.p + ta * p.a_tile + (size_t)kb0 * 8 * 8192, p.a.ld, p.a.rows, p.a.cols};
+  const OpRef bo{p.b.p + tb * p.b_tile + (size_t)kb0 * TILE * p.b.ld, p.b.ld,
+                 p.b.rows - kb0 * TILE, p.b.cols - tb * TILE};
+  const int* kf = SKIP ? p.kflags + (size_t)ta * p.fa + (size_t)kb0 * p.fk : nullptr;
   floatx16 acc[4][4];
   if (!second)
-    gemm_tile<VEC, SKIP, false, OP_BLK, OP_KROW>(a, bo, p.K, kf, p.fk, sm, acc);
+    gemm_tile<VEC, SKIP, false, OP_BLK, OP_KROW>(a, bo, (kb1 - kb0) * TILE, kf, p.fk, sm, acc);
   else
     gemm_tile<VEC, SKIP, false, OP_KBLK, OP_KROW>(a, bo, p.K, kf, p.fk, sm, acc);
-  const bool accum = p.accum != 0;
+  const bool accum = p.accum != 0 && part == 0;
+  float* const Cb = part == 0 ? p.C : p.P + (size_t)(part - 1) * p.p_part;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = ta * TILE + wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
       if (row >= p.c_rows) continue;
-      float* crow = p.C + (size_t)row * p.ldc;
+      float* crow = Cb + (size_t)row * p.ldc;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int col = tb * TILE + wj * 128 + jj * 32 + (lane & 31);
@@ -231,6 +255,96 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 }
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
+
+// C[i] += P[0][i] + P[1][i] + ... (parts - 1 partials, in that order), over the
+// n = rows * ld elements of C; four consecutive elements per thread (n % 4 == 0,
+// 16-byte aligned).
+__global__ __launch_bounds__(256) void k_split_reduce4(float* __restrict__ C,
+                                                       const float* __restrict__ P, size_t part,
+                                                       int nparts, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 c = reinterpret_cast<const float4*>(C)[i];
+  for (int q = 0; q < nparts; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(P + (size_t)q * part)[i];
+    c.x += v.x;
+    c.y += v.y;
+    c.z += v.z;
+    c.w += v.w;
+  }
+  reinterpret_cast<float4*>(C)[i] = c;
+}
+
+__global__ __launch_bounds__(256) void k_split_reduce1(float* __restrict__ C,
+                                                       const float* __restrict__ P, size_t part,
+                                                       int nparts, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float c = C[i];
+  for (int q = 0; q < nparts; ++q) c += P[(size_t)q * part + i];
+  C[i] = c;
+}
+
+// Split of the dh contraction over K: the K-part count for one vocab chunk of
+// nvt tiles, chosen by simulating the hardware's in-order dispatch of the
+// launch (dh tasks first, each to the earliest free CU, then dW tasks) with a
+// cost of one unit per 32-wide K slice plus a fixed per-task overhead, and
+// adding the reduction's memory time.  Splitting pays when dh has few output
+// tiles (small M).  The model is optimistic for large tiles (at the Gemma-4B
+// shape without dW it predicts 17 % for two parts; 4 % was measured, as a
+// quarter-full second round runs at a higher clock), so a split is taken only
+// for a predicted gain of 20 % or more.
+static int dh_split_sim(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D,
+                        int max_parts) {
+  const long long nT = (long long)nMt * nDt;
+  const double over = 8.0, slice_us = 0.9, reduce_bps = 4.0e6;  // bytes per us
+  double best = 0.0;
+  int best_ks = 1;
+  for (int ks = 1; ks <= max_parts && ks <= nvt; ++ks) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> q(
+        std::greater<double>(), std::vector<double>(kCUs, 0.0));
+    auto run = [&](double cost) {
+      const double t = q.top();
+      q.pop();
+      q.push(t + cost);
+    };
+    for (long long t = 0; t < nT; ++t)
+      for (int part = 0; part < ks; ++part) {
+        const int blocks = (part + 1) * nvt / ks - part * nvt / ks;
+        run(blocks * (kTile / 32) + over);
+      }
+    if (with_dw)
+      for (long long t = 0; t < (long long)nvt * nDt; ++t) run(Mpad / 32 + over);
+    double span = 0.0;
+    while (!q.empty()) {
+      span = q.top();
+      q.pop();
+    }
+    if (ks > 1) span += (double)(ks + 1) * M * D * 4.0 / reduce_bps / slice_us;
+    if (ks == 1 || span < best * 0.8) {
+      best = span;
+      best_ks = ks;
+    }
+  }
+  return best_ks;
+}
+
+int dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D, int max_parts) {
+  if (max_parts <= 1 || (long long)nMt * nDt >= 4LL * kCUs || nvt < 2) return 1;
+  // the simulation takes up to milliseconds: one run per distinct shape
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, bool, int, int, int, int>, int> memo;
+  const auto key = std::make_tuple(nMt, nDt, nvt, with_dw, Mpad, M, D, max_parts);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto it = memo.find(key);
+    if (it != memo.end()) return it->second;
+  }
+  const int ks = dh_split_sim(nMt, nDt, nvt, with_dw, Mpad, M, D, max_parts);
+  std::lock_guard<std::mutex> g(mu);
+  memo.emplace(key, ks);
+  return ks;
+}
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   hipError_t e;
@@ -276,14 +390,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     {
       const bool skip = a.block_eps > 0.f;
       const int fstride = a.Vc / kTile;
+      const bool with_dw = a.q.Wq == nullptr;
+      const int ks = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.M, a.D, a.P_parts + 1);
       GemmProb dh{OpRef{a.G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
                   (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt,
-                  pad8(a.nMt * nDt), a.flags, fstride, 1, v0 == 0 ? 0 : 1};
+                  pad8(a.nMt * nDt * ks), a.flags, fstride, 1, v0 == 0 ? 0 : 1, ks, a.P,
+                  (size_t)a.M * a.D};
       GemmProb dw{OpRef{a.G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
-                  (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen, a.D, nvt, nDt,
-                  pad8(nvt * nDt), a.flags, 1, fstride, 0};
+                  (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
+                  a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nullptr, 0};
       // the quantised head is frozen: dh only
-      const dim3 grid(a.q.Wq ? dh.nl : dh.nl + dw.nl);
+      const dim3 grid(with_dw ? dh.nl + dw.nl : dh.nl);
       if (a.vec) {
         if (skip) hipLaunchKernelGGL((k_grads<true, true>), grid, dim3(NT), 0, st, dh, dw);
         else hipLaunchKernelGGL((k_grads<false, true>), grid, dim3(NT), 0, st, dh, dw);
@@ -292,6 +409,17 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
         else hipLaunchKernelGGL((k_grads<false, false>), grid, dim3(NT), 0, st, dh, dw);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (ks > 1) {
+        const size_t n = (size_t)a.M * a.D;
+        if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.dh) & 15u) == 0) {
+          hipLaunchKernelGGL(k_split_reduce4, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                             st, a.dh, a.P, n, ks - 1, n / 4);
+        } else {
+          hipLaunchKernelGGL(k_split_reduce1, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                             a.dh, a.P, n, ks - 1, n);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   }
   return hipSuccess;

@@ -15,6 +15,8 @@ constexpr int kTile = 256;
 constexpr int kVocabChunk = 16384;
 // Doubles per pair in the epilogue's pair table.
 constexpr int kPairStride = 16;
+// Compute units of the target chip (MI355X): the workgroups one launch round holds.
+constexpr int kCUs = 256;
 
 struct FwdArgs {
   const u16* H;
@@ -112,7 +114,12 @@ struct BwdArgs {
   // null, or the forward's saved block maximum ([ceil(V / 256), M]): with
   // block_eps > 0 a tile's skip is decided from it before its recompute
   const float* bm;
+  // split-K partials of the dh contraction: P_parts buffers of M x D fp32
+  float* P;
+  int P_parts;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
+// K parts of one chunk's dh contraction (1 = none), at most max_parts.
+int dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D, int max_parts);
 
 }  // namespace cce

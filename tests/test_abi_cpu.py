@@ -58,6 +58,16 @@ def test_workspace_is_independent_of_V():
     assert B.workspace_bytes(1 << 22, 10, 10) == 0
 
 
+def test_workspace_small_M_bounded():
+    """Small M reserves split-K partials of dh, within half the gradient chunk."""
+    for M, D in ((1279, 2048), (1024, 4096), (300, 64)):
+        ws = B.workspace_bytes(M, 262144, D)
+        Mpad = (M + 255) // 256 * 256
+        g = 2 * Mpad * 16384
+        assert g <= ws <= g + g // 2 + 4 * 1024 * 1024
+        assert ws == B.workspace_bytes(M, 1 << 20, D)
+
+
 def test_workspace_bound_at_gemma_and_stress():
     # the bf16 gradient chunk G dominates: 2 * Mpad * 16384 bytes, plus < 2 MB per 8192 rows
     gemma = B.workspace_bytes(8192, 262144, 2560)
@@ -152,8 +162,11 @@ def test_quant_workspace_adds_one_chunk_buffer():
     sizes = [B.workspace_bytes_q(M, V, D) for V in (32768, 262144, 1 << 20)]
     assert len(set(sizes)) == 1
     extra = sizes[0] - B.workspace_bytes(M, 262144, D)
-    # the bf16 chunk of the dequantised head (16384 x D) and two fp32 rows of Mpad
-    assert 2 * 16384 * D + 8 * M <= extra < 2 * 16384 * D + 8 * M + 3 * 256
+    # the bf16 chunk of the dequantised head (16384 x D), two fp32 rows of Mpad, and
+    # at most 7 fp32 M x D partial buffers of the split dh contraction
+    assert 2 * 16384 * D + 8 * M <= extra <= 2 * 16384 * D + 8 * M + 7 * M * D * 4 + 4 * 256
+    # the partials stay within half the gradient chunk
+    assert sizes[0] <= B.workspace_bytes(M, 262144, D) + 2 * 16384 * D + 8 * M + 8192 * 16384 + 4 * 256
     assert B.workspace_bytes_q(0, 10, 64) == 0
 
 

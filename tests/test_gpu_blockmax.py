@@ -141,7 +141,8 @@ def test_backward_skip_from_block_max(device, case):
 def test_quant_head_block_max(device):
     """The quantised head's forward writes the same block maximum as the bf16
     head on its dequantised values, and its dh with the stored skip equals the
-    bf16 backward's byte for byte."""
+    bf16 backward's up to the order of fp32 sums (its dh may split K
+    differently: the frozen head has no dW)."""
     spans, D, V = [(10, 200, 190, 16)], 128, 17000
     wl = WL.make_custom(spans, D=D, V=V, seed=700, w_std=0.05)
     dead_structure(wl, np.arange(1024, 1536), sink=-3.0)
@@ -170,7 +171,7 @@ def test_quant_head_block_max(device):
     dh_q = hq.backward_q(h, Wq, sd, bd, 8, 64, y, lse, coef, 0.0, eps, block_max=bm_q)
     dh_b, _ = hb.backward(h, Wb, y, lse, coef, 0.0, eps, block_max=bm_b)
     torch.cuda.synchronize()
-    assert dh_q.cpu().numpy().tobytes() == dh_b.cpu().numpy().tobytes()
+    assert rel_l2(dh_q.cpu().numpy(), dh_b.cpu().numpy().astype(np.float64)) <= 1e-6
     check_block_max(bm_q.cpu().numpy(), O.block_max(wl.h64(), Wo), "quantised block_max")
 
 

@@ -5,7 +5,7 @@ The oracle's quantised head is round_bf16(dequantize(codes, scales, biases)):
 the value s * q + b, taken in bf16 for the contractions.  Gates as for the bf16
 head: logp / lse relative error <= 1e-3 per row, dh relative L2 <= 1e-2; the
 quantised backward also equals the bf16 backward on the same (dequantised,
-bf16) head byte for byte, since both run the same kernels in the same order.
+bf16) head up to the order of fp32 sums.
 """
 import sys
 
@@ -110,14 +110,15 @@ def test_quant_forward_backward(device, case):
     assert e <= RTOL_GRAD
     assert np.all(dh.cpu().numpy()[~ok] == 0.0)
 
-    # the bf16 path on the same head (uploaded as bf16) gives the same dh bytes
+    # the bf16 path on the same head (uploaded as bf16) gives the same dh up to the
+    # order of the fp32 sums (the frozen head's dh contraction may split K differently)
     Wb = B.to_device_bits(WL.f32_to_bf16_bits(Wo.astype(np.float32)), device)
     head_b = B.Head(wl.M, V, D, device)
     dh_b, _ = head_b.backward(h, Wb, y, lse, torch.from_numpy(coef).to(device), feps, feps,
                               softcap=cap)
     lp_b, lse_b = head_b.forward(h, Wb, y, softcap=cap)
     torch.cuda.synchronize()
-    assert dh_b.cpu().numpy().tobytes() == dh.cpu().numpy().tobytes()
+    assert rel_l2(dh.cpu().numpy(), dh_b.cpu().numpy().astype(np.float64)) <= 1e-6
     # the forward folds chunks in another order: equal to rounding
     np.testing.assert_allclose(lse_b.cpu().numpy(), lse_g, rtol=1e-6, atol=1e-6)
 
