@@ -256,9 +256,9 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
 
-// C[i] += P[0][i] + P[1][i] + ... (parts - 1 partials, in that order), over the
-// n = rows * ld elements of C; four consecutive elements per thread (n % 4 == 0,
-// 16-byte aligned).
+// C[i] += P[0][i] + P[1][i] + ... + P[nparts-1][i] (partial q at P + q * part),
+// added in that order, over the n elements of C.  The 4-wide variant takes four
+// consecutive elements per thread (n % 4 == 0, C and P 16-byte aligned).
 __global__ __launch_bounds__(256) void k_split_reduce4(float* __restrict__ C,
                                                        const float* __restrict__ P, size_t part,
                                                        int nparts, size_t n4) {

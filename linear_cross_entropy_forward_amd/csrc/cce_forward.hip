@@ -238,11 +238,14 @@ static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int
 }
 
 void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {
-  const long long tiles = (long long)nMt * nVt;
-  long long t = (tiles + 255) / 256;
-  if (t < 1) t = 1;
-  T = (int)t;
-  S = (int)((nVt + t - 1) / t);
+  // as many splits per token tile as one round of kCUs workgroups holds (a
+  // second, nearly empty round would double the time), then the fewest splits
+  // for that many tiles per workgroup
+  int smax = kCUs / nMt;
+  if (smax < 1) smax = 1;
+  if (smax > nVt) smax = nVt;
+  T = (nVt + smax - 1) / smax;
+  S = (nVt + T - 1) / T;
 }
 
 hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {

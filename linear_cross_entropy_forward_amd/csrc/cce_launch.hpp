@@ -37,8 +37,8 @@ struct FwdArgs {
   float* bm;
 };
 hipError_t launch_forward(const FwdArgs& a, hipStream_t st);
-// Forward split: T vocab tiles per workgroup so that nMt * S workgroups cover
-// nVt tiles in about one round of 256 workgroups (one per CU).
+// Forward split: S workgroups per token tile, T vocab tiles each, with
+// nMt * S <= kCUs (one round, one workgroup per CU) when nMt <= kCUs.
 void fwd_split_tiles(int nMt, int nVt, int& S, int& T);
 // The forward's tile launches (full tiles, then a ragged last tile) writing
 // `slots` partial (max, sum-exp) slots, and the final merge of `slots` slots.
