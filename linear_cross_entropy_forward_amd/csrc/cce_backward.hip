@@ -33,6 +33,49 @@
 
 namespace cce {
 
+// The gradient entries of one recomputed tile, straight from the accumulators
+// to G: per (ii, jj, q) a lane holds 4 consecutive vocab entries of one token,
+// 8 bytes of one row of the block (vocab block wi*4 + ii of the tile).  !CAP:
+// acc holds the raw logits and the softmax entry exp(z - lse) is formed here;
+// CAP: acc holds t = tanh(z / c).  TGT: some token of this wave has its target
+// among the wave's vocab rows (else no entry is compared with the target);
+// VT: the tile runs past the chunk's last vocab row (those entries are 0).
+template <bool CAP, bool FILTER, bool TGT, bool VT>
+__device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[4][4],
+                                                const float (&nlse)[4], const float (&cf)[4],
+                                                const int (&off)[4], float c1, float filter_eps,
+                                                int vl0, int vlen, int half, int wj, int lane,
+                                                u16* __restrict__ gt) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int tj = wj * 128 + jj * 32 + (lane & 31);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vbad = VT && (vl0 + ii * 32 + 8 * q + 4 * half + e >= vlen);
+          float p, sech2 = 1.f;
+          if (CAP) {
+            const float t = acc[ii][jj][4 * q + e];
+            p = vbad ? 0.f : fast_exp2(fmaf(t, c1, nlse[jj]));
+            sech2 = 1.f - t * t;
+          } else {
+            p = fast_exp2(fmaf(acc[ii][jj][4 * q + e], LOG2E, nlse[jj]));
+            if (vbad) p = 0.f;
+          }
+          const bool is_t = TGT && (off[jj] == ii * 32 + 8 * q + e);
+          if (FILTER && p < filter_eps && !is_t) p = 0.f;
+          g[e] = cf[jj] * (is_t ? p - 1.f : p) * sech2;
+        }
+        *reinterpret_cast<u32x2*>(gt + (size_t)ii * 8192 + tj * 32 + 8 * q) =
+            u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+      }
+  }
+}
+
 // Recompute one 256 (vocab) x 256 (token) logit tile of the chunk and write
 // its gradient tile.  A = W rows of the chunk, B = h rows, so each lane owns
 // one token (lse, coef, target in registers) and 16 vocab entries per MFMA
@@ -98,37 +141,44 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
     const int o = (yy >= 0) ? yy - (v0 + vl0) : -1;
     any_tgt_lane |= (unsigned)o < 128u;
   }
-  // softmax entries into acc (CAP: tanh(z / c)); rows beyond the chunk's
-  // valid vocab become 0 (CAP: they are masked again at the store)
+  // CAP: acc becomes tanh(z / c) (rows beyond the chunk's valid vocab are
+  // masked at the store).  The largest softmax entry is formed only for the
+  // recompute-time skip test; otherwise the store pass forms each entry once.
   const bool vtail = vt * TILE + TILE > vlen;
+  const bool skip_test = block_eps > 0.f && !bm;
   const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;
   const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
   float pmax = 0.f;
-  float tmax[4] = {-1.f, -1.f, -1.f, -1.f};
+  if (CAP) {
+    float tmax[4] = {-1.f, -1.f, -1.f, -1.f};
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool vbad = vtail && (vl0 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= vlen);
+      for (int r = 0; r < 16; ++r) {
+        const bool vbad = vtail && (vl0 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= vlen);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (CAP) {
+        for (int jj = 0; jj < 4; ++jj) {
           const float t = tanh_scaled(acc[ii][jj][r], k2);
           acc[ii][jj][r] = t;
           if (!vbad) tmax[jj] = fmaxf(tmax[jj], t);
-        } else {
-          float p = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nlse[jj]));
-          if (vbad) p = 0.f;
-          acc[ii][jj][r] = p;
-          pmax = fmaxf(pmax, p);
         }
       }
-    }
-  if (CAP) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) pmax = fmaxf(pmax, fast_exp2(fmaf(tmax[jj], c1, nlse[jj])));
+  } else if (skip_test) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool vbad = vtail && (vl0 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= vlen);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float p = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nlse[jj]));
+          if (!vbad) pmax = fmaxf(pmax, p);
+        }
+      }
   }
-  if (block_eps > 0.f && !bm) {
+  if (skip_test) {
     // skip the tile if every softmax entry is below block_eps and no token of
     // the tile has its target among the tile's vocab rows
     const bool keep_lane = pmax >= block_eps || any_tgt_lane;
@@ -143,38 +193,17 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
   }
   if (tid == 0) *flag = 1;
 
-  // The gradient tile goes straight from the accumulators to G: per (ii, jj,
-  // q) a lane holds 4 consecutive vocab entries of one token, 8 bytes of
-  // one row of the block (vocab block wi*4 + ii of the tile).
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
   u16* gt = G + ((size_t)mt * nkbV + vt * 8 + wi * 4) * 8192 + 4 * half;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int tj = wj * 128 + jj * 32 + (lane & 31);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float p, sech2 = 1.f;
-          if (CAP) {
-            const float t = acc[ii][jj][4 * q + e];
-            const bool vbad = vtail && (vl0 + ii * 32 + 8 * q + 4 * half + e >= vlen);
-            p = vbad ? 0.f : fast_exp2(fmaf(t, c1, nlse[jj]));
-            sech2 = 1.f - t * t;
-          } else {
-            p = acc[ii][jj][4 * q + e];
-          }
-          const bool is_t = wave_has_tgt && (off[jj] == ii * 32 + 8 * q + e);
-          if (FILTER && p < filter_eps && !is_t) p = 0.f;
-          g[e] = cf[jj] * (is_t ? p - 1.f : p) * sech2;
-        }
-        *reinterpret_cast<u32x2*>(gt + (size_t)ii * 8192 + tj * 32 + 8 * q) =
-            u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-      }
+#define CCE_STORE(TGT, VT)                                                                  \
+  store_grad_tile<CAP, FILTER, TGT, VT>(acc, nlse, cf, off, c1, filter_eps, vl0, vlen, half, wj, \
+                                        lane, gt)
+  if (wave_has_tgt) {
+    if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
+  } else {
+    if (vtail) CCE_STORE(false, true); else CCE_STORE(false, false);
   }
+#undef CCE_STORE
 }
 
 // One fp32-output contraction C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k]
