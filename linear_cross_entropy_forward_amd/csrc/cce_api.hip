@@ -38,24 +38,25 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
   size_t part_m, part_s, tgt, pairs, g, flags;
-  size_t psplit;  // split-K partials of dh (psplit_parts buffers of M x D fp32)
-  int psplit_parts;
+  size_t psplit;  // split-K partial tiles of dh (psplit_tiles of 256 x 256 fp32)
+  long long psplit_tiles;
   size_t total;
   // quantised head only: running (max, sum-exp), the bf16 chunk buffer and its
   // own dh partials (no dW there, so dh splits further)
   size_t run_m, run_s, wbuf, psplit_q;
-  int psplit_parts_q;
+  long long psplit_tiles_q;
   size_t total_q;
 };
 
-// dh split-K partial buffers reserved for a full vocab chunk: as many as the
-// split schedule wants, within half the gradient chunk's bytes.
-int split_parts(const Layout& L, int64_t M, int64_t D, bool with_dw) {
-  const size_t one = (size_t)M * D * 4;
-  const size_t cap = (size_t)L.Mpad * L.Vc * 2 / 2;
-  const int max_parts = (int)std::min<size_t>(7, cap / one);
-  return cce::dh_split((int)L.nMt, (int)(L.Dpad / kTile), (int)(L.Vc / kTile), with_dw,
-                       (int)L.Mpad, (int)M, (int)D, max_parts + 1) - 1;
+// dh split-K partial tiles reserved for a full vocab chunk: as many as its
+// split schedule needs, within half the gradient chunk's bytes.
+long long split_tiles(const Layout& L, bool with_dw) {
+  const long long tile = (long long)kTile * kTile * 4;
+  const long long cap = (long long)L.Mpad * L.Vc * 2 / 2 / tile;
+  const int nMt = (int)L.nMt, nDt = (int)(L.Dpad / kTile);
+  const cce::DhSplit sp =
+      cce::dh_split(nMt, nDt, (int)(L.Vc / kTile), with_dw, (int)L.Mpad, cap);
+  return (long long)(sp.ks - 1) * ((long long)nMt * nDt - sp.n_full);
 }
 
 Layout layout(int64_t M, int64_t V, int64_t D) {
@@ -78,15 +79,15 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   const size_t base = off;
-  L.psplit_parts = split_parts(L, M, D, true);
-  L.psplit = take((size_t)L.psplit_parts * M * D * 4);
+  L.psplit_tiles = split_tiles(L, true);
+  L.psplit = take((size_t)L.psplit_tiles * kTile * kTile * 4);
   L.total = off;
   off = base;  // the quantised layout does not use the bf16 head's partials
   L.run_m = take((size_t)L.Mpad * sizeof(float));
   L.run_s = take((size_t)L.Mpad * sizeof(float));
   L.wbuf = take((size_t)L.Vc * D * 2);
-  L.psplit_parts_q = split_parts(L, M, D, false);
-  L.psplit_q = take((size_t)L.psplit_parts_q * M * D * 4);
+  L.psplit_tiles_q = split_tiles(L, false);
+  L.psplit_q = take((size_t)L.psplit_tiles_q * kTile * kTile * 4);
   L.total_q = off;
   return L;
 }
@@ -273,7 +274,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.status = dev_status;
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit);
-  a.P_parts = L.psplit_parts;
+  a.P_tiles = L.psplit_tiles;
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
 }
@@ -371,7 +372,7 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
   a.status = dev_status;
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit_q);
-  a.P_parts = L.psplit_parts_q;
+  a.P_tiles = L.psplit_tiles_q;
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
   a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);

@@ -211,11 +211,13 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
 // tile ta of A starts a_tile elements after a.p, tile tb of B b_tile elements
 // after b.p (with b.cols reduced by tb*256).
 //
-// Split K (first problem only, the dh form: A blocked, B read transposed):
-// with ks > 1 every output tile is ks tasks, part q taking K blocks
-// [q*nb/ks, (q+1)*nb/ks) of the nb = K/256; part 0 writes C as above, part q > 0
-// writes (no accumulation) the partial tile P + (q-1)*p_part (leading dimension
-// ldc), and a later reduction adds the partials to C in the order q = 1, 2, ...
+// Split K (first problem only, the dh form: A blocked, B read transposed): the
+// tiles of raster index >= n_full are each ks tasks, part q taking K blocks
+// [q*nb/ks, (q+1)*nb/ks) of the nb = K/256 (tiles below n_full are one task
+// over all of K).  Part 0 writes C as above; part q > 0 of split tile u writes
+// (no accumulation) the 256 x 256 partial tile P + ((q-1)*nsplit + u)*65536
+// (tile-local, leading dimension 256), and k_split_reduce adds the partials to
+// C in the order q = 1, 2, ...  Tasks run full tiles first, then the parts.
 struct GemmProb {
   OpRef a, b;
   size_t a_tile, b_tile;
@@ -225,11 +227,43 @@ struct GemmProb {
   int nA, nB, nl;
   const int* kflags;  // per 256-wide K block of A tile ta: kflags[ta*fa + kb*fk]
   int fa, fk;
-  int accum;  // 1: C += result, 0: C = result
-  int ks;     // K parts (1: no split)
+  int accum;   // 1: C += result, 0: C = result
+  int ks;      // K parts of a split tile (1: no split)
+  int n_full;  // tiles (raster order) that are not split
   float* P;
-  size_t p_part;
 };
+
+// Workgroup b of a problem -> (tile, K part, split-tile index u or -1); false
+// for the padding workgroups.  Unsplit: the XCD-contiguous grouped raster of
+// map_tile.  Split (n_full a multiple of 8): each XCD (b % 8) takes its eighth
+// of the full tiles first and then its eighth of the parts, so the long tasks
+// are spread over all XCDs.
+__device__ __forceinline__ bool split_task(const GemmProb& p, int b, int& ta, int& tb, int& part,
+                                           int& u) {
+  const int nT = p.nA * p.nB;
+  int L;
+  part = 0;
+  u = -1;
+  if (p.ks == 1) {
+    L = xcd_task(b, p.nl);
+    if (L >= nT) return false;
+  } else {
+    const int x = b & 7, i = b >> 3;
+    const int nf8 = p.n_full / 8;
+    if (i < nf8) {
+      L = x * nf8 + i;
+    } else {
+      const int np = (nT - p.n_full) * p.ks, np8 = (np + 7) / 8;
+      const int r = x * np8 + (i - nf8);
+      if (i - nf8 >= np8 || r >= np) return false;
+      u = r / p.ks;
+      part = r - u * p.ks;
+      L = p.n_full + u;
+    }
+  }
+  raster_tile(L, p.nA, p.nB, 8, ta, tb);
+  return true;
+}
 
 // The dh and dW contractions of one vocab chunk in a single launch: workgroups
 // [0, p0.nl) take p0 (dh, the longer K), the rest take p1 (dW).  Dispatching
@@ -244,14 +278,13 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
   const bool second = b >= p0.nl;
   const GemmProb p = second ? p1 : p0;
   if (second) b -= p0.nl;
-  int ta, tb;
-  if (!map_tile(b, p.nl, p.nA, p.nB * p.ks, 8, ta, tb)) return;
-  const int part = tb / p.nB;  // K part (0 unless the problem is split)
-  tb -= part * p.nB;
+  int ta, tb, part, u;
+  if (!split_task(p, b, ta, tb, part, u)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   const int nb = p.K / TILE;
-  const int kb0 = part * nb / p.ks, kb1 = (part + 1) * nb / p.ks;
+  const int parts = u < 0 ? 1 : p.ks;
+  const int kb0 = part * nb / parts, kb1 = (part + 1) * nb / parts;
   // part offsets (the split problem is of the dh form: A blocked, 8 blocks of
   // 8192 elements per 256 K; B [k][i] with pitch ld)
   const OpRef a{p.a.p + ta * p.a_tile + (size_t)kb0 * 8 * 8192, p.a.ld, p.a.rows, p.a.cols};
@@ -264,7 +297,22 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
   else
     gemm_tile<VEC, SKIP, false, OP_KBLK, OP_KROW>(a, bo, p.K, kf, p.fk, sm, acc);
   const bool accum = p.accum != 0 && part == 0;
-  float* const Cb = part == 0 ? p.C : p.P + (size_t)(part - 1) * p.p_part;
+  if (part > 0) {
+    // a partial tile, tile-local (rows and columns past C's are never read)
+    const int nsplit = p.nA * p.nB - p.n_full;
+    float* const Pt = p.P + ((size_t)(part - 1) * nsplit + u) * (TILE * TILE);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          Pt[(size_t)row * TILE + wj * 128 + jj * 32 + (lane & 31)] = acc[ii][jj][r];
+      }
+    return;
+  }
+  float* const Cb = p.C;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
@@ -285,51 +333,44 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
 
-// C[i] += P[0][i] + P[1][i] + ... + P[nparts-1][i] (partial q at P + q * part),
-// added in that order, over the n elements of C.  The 4-wide variant takes four
-// consecutive elements per thread (n % 4 == 0, C and P 16-byte aligned).
-__global__ __launch_bounds__(256) void k_split_reduce4(float* __restrict__ C,
-                                                       const float* __restrict__ P, size_t part,
-                                                       int nparts, size_t n4) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  float4 c = reinterpret_cast<const float4*>(C)[i];
-  for (int q = 0; q < nparts; ++q) {
-    const float4 v = reinterpret_cast<const float4*>(P + (size_t)q * part)[i];
-    c.x += v.x;
-    c.y += v.y;
-    c.z += v.z;
-    c.w += v.w;
+// For each split tile u of p, C[tile] += P[0][u] + P[1][u] + ... + P[ks-2][u],
+// the partials added in that order.  Workgroup (u, y) takes tile rows
+// 16y .. 16y+15, one column per thread (each row a coalesced 1 KB).
+__global__ __launch_bounds__(256) void k_split_reduce(GemmProb p) {
+  const int nsplit = p.nA * p.nB - p.n_full;
+  const int u = blockIdx.x;
+  if (u >= nsplit) return;
+  int ta, tb;
+  raster_tile(p.n_full + u, p.nA, p.nB, 8, ta, tb);
+  const int col = tb * TILE + (int)threadIdx.x;
+  if (col >= p.c_cols) return;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = (int)blockIdx.y * 16 + k;
+    const int row = ta * TILE + r;
+    if (row < p.c_rows) {
+      float c = p.C[(size_t)row * p.ldc + col];
+      for (int q = 0; q < p.ks - 1; ++q)
+        c += p.P[((size_t)q * nsplit + u) * (TILE * TILE) + (size_t)r * TILE + threadIdx.x];
+      p.C[(size_t)row * p.ldc + col] = c;
+    }
   }
-  reinterpret_cast<float4*>(C)[i] = c;
 }
 
-__global__ __launch_bounds__(256) void k_split_reduce1(float* __restrict__ C,
-                                                       const float* __restrict__ P, size_t part,
-                                                       int nparts, size_t n) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float c = C[i];
-  for (int q = 0; q < nparts; ++q) c += P[(size_t)q * part + i];
-  C[i] = c;
-}
-
-// Split of the dh contraction over K: the K-part count for one vocab chunk of
-// nvt tiles, chosen by simulating the hardware's in-order dispatch of the
-// launch (dh tasks first, each to the earliest free CU, then dW tasks) with a
-// cost of one unit per 32-wide K slice plus a fixed per-task overhead, and
-// adding the reduction's memory time.  Splitting pays when dh has few output
-// tiles (small M).  The model is optimistic for large tiles (at the Gemma-4B
-// shape without dW it predicts 17 % for two parts; 4 % was measured, as a
-// quarter-full second round runs at a higher clock), so a split is taken only
-// for a predicted gain of 20 % or more.
-static int dh_split_sim(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D,
-                        int max_parts) {
+// Split of the dh contraction over K for one vocab chunk of nvt tiles: either
+// every tile in ks parts (n_full = 0), or only the tiles past the last full
+// round of kCUs (a quarter-full second round of long tasks otherwise idles most
+// of the chip).  Chosen by simulating the hardware's in-order dispatch of the
+// launch (full tiles, then the parts, then the dW tasks, each to the earliest
+// free CU) with a cost of one unit per 32-wide K slice plus a fixed per-task
+// overhead, and adding the reduction's memory time; the partial tiles must fit
+// max_tiles.  The model is optimistic (a quarter-full round also runs at a
+// higher clock), so a split is taken only for a predicted gain of 20 % or more.
+static DhSplit dh_split_sim(int nMt, int nDt, int nvt, bool with_dw, int Mpad, long long max_tiles) {
   const long long nT = (long long)nMt * nDt;
-  const double over = 8.0, slice_us = 0.9, reduce_bps = 4.0e6;  // bytes per us
-  double best = 0.0;
-  int best_ks = 1;
-  for (int ks = 1; ks <= max_parts && ks <= nvt; ++ks) {
+  const double over = 8.0, unit_us = 0.9, reduce_bpu = 4.0e6 * unit_us;  // bytes per unit
+  const double tile_bytes = (double)kTile * kTile * 4;
+  auto span_of = [&](long long n_full, int ks) {
     std::priority_queue<double, std::vector<double>, std::greater<double>> q(
         std::greater<double>(), std::vector<double>(kCUs, 0.0));
     auto run = [&](double cost) {
@@ -337,11 +378,10 @@ static int dh_split_sim(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M
       q.pop();
       q.push(t + cost);
     };
-    for (long long t = 0; t < nT; ++t)
-      for (int part = 0; part < ks; ++part) {
-        const int blocks = (part + 1) * nvt / ks - part * nvt / ks;
-        run(blocks * (kTile / 32) + over);
-      }
+    for (long long t = 0; t < n_full; ++t) run(nvt * (kTile / 32) + over);
+    for (long long t = n_full; t < nT; ++t)
+      for (int part = 0; part < ks; ++part)
+        run(((part + 1) * nvt / ks - part * nvt / ks) * (kTile / 32) + over);
     if (with_dw)
       for (long long t = 0; t < (long long)nvt * nDt; ++t) run(Mpad / 32 + over);
     double span = 0.0;
@@ -349,30 +389,43 @@ static int dh_split_sim(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M
       span = q.top();
       q.pop();
     }
-    if (ks > 1) span += (double)(ks + 1) * M * D * 4.0 / reduce_bps / slice_us;
-    if (ks == 1 || span < best * 0.8) {
-      best = span;
-      best_ks = ks;
+    if (n_full < nT) span += (double)(nT - n_full) * tile_bytes * (ks + 1) / reduce_bpu;
+    return span;
+  };
+  DhSplit best{1, (int)nT};
+  const double none = span_of(nT, 1);
+  double best_span = none;
+  const long long tails[2] = {0, nT > kCUs ? nT - nT % kCUs : nT};
+  for (long long n_full : tails) {
+    if (n_full >= nT) continue;
+    for (int ks = 2; ks <= 8 && ks <= nvt; ++ks) {
+      if ((long long)(ks - 1) * (nT - n_full) > max_tiles) break;
+      const double sp = span_of(n_full, ks);
+      if (sp < 0.8 * none && sp < best_span) {
+        best_span = sp;
+        best = DhSplit{ks, (int)n_full};
+      }
     }
   }
-  return best_ks;
+  return best;
 }
 
-int dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D, int max_parts) {
-  if (max_parts <= 1 || (long long)nMt * nDt >= 4LL * kCUs || nvt < 2) return 1;
+DhSplit dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, long long max_tiles) {
+  const long long nT = (long long)nMt * nDt;
+  if (max_tiles <= 0 || nT >= 4LL * kCUs || nvt < 2) return DhSplit{1, (int)nT};
   // the simulation takes up to milliseconds: one run per distinct shape
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, bool, int, int, int, int>, int> memo;
-  const auto key = std::make_tuple(nMt, nDt, nvt, with_dw, Mpad, M, D, max_parts);
+  static std::map<std::tuple<int, int, int, bool, int, long long>, DhSplit> memo;
+  const auto key = std::make_tuple(nMt, nDt, nvt, with_dw, Mpad, max_tiles);
   {
     std::lock_guard<std::mutex> g(mu);
     const auto it = memo.find(key);
     if (it != memo.end()) return it->second;
   }
-  const int ks = dh_split_sim(nMt, nDt, nvt, with_dw, Mpad, M, D, max_parts);
+  const DhSplit r = dh_split_sim(nMt, nDt, nvt, with_dw, Mpad, max_tiles);
   std::lock_guard<std::mutex> g(mu);
-  memo.emplace(key, ks);
-  return ks;
+  memo.emplace(key, r);
+  return r;
 }
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
@@ -420,14 +473,16 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       const bool skip = a.block_eps > 0.f;
       const int fstride = a.Vc / kTile;
       const bool with_dw = a.q.Wq == nullptr;
-      const int ks = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.M, a.D, a.P_parts + 1);
+      const DhSplit sp = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.P_tiles);
+      const int nT = a.nMt * nDt;
+      const int dh_nl = sp.ks == 1 ? pad8(nT)
+                                   : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
       GemmProb dh{OpRef{a.G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
-                  (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt,
-                  pad8(a.nMt * nDt * ks), a.flags, fstride, 1, v0 == 0 ? 0 : 1, ks, a.P,
-                  (size_t)a.M * a.D};
+                  (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, dh_nl, a.flags,
+                  fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P};
       GemmProb dw{OpRef{a.G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
                   (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
-                  a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nullptr, 0};
+                  a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr};
       // the quantised head is frozen: dh only
       const dim3 grid(with_dw ? dh.nl + dw.nl : dh.nl);
       if (a.vec) {
@@ -438,15 +493,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
         else hipLaunchKernelGGL((k_grads<false, false>), grid, dim3(NT), 0, st, dh, dw);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (ks > 1) {
-        const size_t n = (size_t)a.M * a.D;
-        if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.dh) & 15u) == 0) {
-          hipLaunchKernelGGL(k_split_reduce4, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
-                             st, a.dh, a.P, n, ks - 1, n / 4);
-        } else {
-          hipLaunchKernelGGL(k_split_reduce1, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                             a.dh, a.P, n, ks - 1, n);
-        }
+      if (sp.n_full < nT) {
+        hipLaunchKernelGGL(k_split_reduce, dim3(nT - sp.n_full, TILE / 16), dim3(256), 0, st, dh);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }

@@ -80,10 +80,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 
 // Launch index -> (ta, tb) tile of an nA x nB tile grid.  Workgroups are dealt
 // to the 8 XCDs round-robin by launch index, so the launch index is first
-// remapped so that each XCD receives a contiguous run of logical tiles; the
-// logical order is a grouped raster (GA 'a' tiles, then the next 'b') so the
-// workgroups sharing one XCD's L2 share both A and B tiles.  The launch grid
-// is padded to a multiple of 8; extra workgroups return false.
+// remapped (xcd_task) so that each XCD receives a contiguous run of logical
+// tiles; the logical order is a grouped raster (GA 'a' tiles, then the next
+// 'b'; raster_tile) so the workgroups sharing one XCD's L2 share both A and B
+// tiles.  The launch grid is padded to a multiple of 8; extra workgroups
+// return false.
+__device__ __forceinline__ int xcd_task(int bid, int nlaunch) {
+  return (bid & 7) * (nlaunch >> 3) + (bid >> 3);
+}
+
 // Logical tile index L -> (ta, tb) in the grouped raster described above.
 __device__ __forceinline__ void raster_tile(int L, int nA, int nB, int GA, int& ta, int& tb) {
   const int ga = GA < nA ? GA : nA;
@@ -97,17 +102,9 @@ __device__ __forceinline__ void raster_tile(int L, int nA, int nB, int GA, int& 
 
 __device__ __forceinline__ bool map_tile(int bid, int nlaunch, int nA, int nB, int GA,
                                          int& ta, int& tb) {
-  const int n = nA * nB;
-  const int per = nlaunch >> 3;
-  const int L = (bid & 7) * per + (bid >> 3);
-  if (L >= n) return false;
-  const int ga = GA < nA ? GA : nA;
-  const int group = L / (ga * nB);
-  const int first = group * ga;
-  const int gsize = (nA - first) < ga ? (nA - first) : ga;
-  const int idx = L - group * ga * nB;
-  ta = first + idx % gsize;
-  tb = idx / gsize;
+  const int L = xcd_task(bid, nlaunch);
+  if (L >= nA * nB) return false;
+  raster_tile(L, nA, nB, GA, ta, tb);
   return true;
 }
 

@@ -114,12 +114,18 @@ struct BwdArgs {
   // null, or the forward's saved block maximum ([ceil(V / 256), M]): with
   // block_eps > 0 a tile's skip is decided from it before its recompute
   const float* bm;
-  // split-K partials of the dh contraction: P_parts buffers of M x D fp32
+  // split-K partials of the dh contraction: room for P_tiles fp32 256 x 256 tiles
   float* P;
-  int P_parts;
+  long long P_tiles;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
-// K parts of one chunk's dh contraction (1 = none), at most max_parts.
-int dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, int M, int D, int max_parts);
+// Split of one chunk's dh contraction: the tiles from raster index n_full on are
+// computed in ks K-parts (ks = 1: no split); (ks - 1) * (tiles - n_full) partial
+// tiles, at most max_tiles.
+struct DhSplit {
+  int ks;
+  int n_full;
+};
+DhSplit dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, long long max_tiles);
 
 }  // namespace cce
