@@ -143,8 +143,6 @@ __device__ __forceinline__ int swz(int row) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ lds_ptr_t to_lds(void* p) { return (lds_ptr_t)(p); }
-
 // LDS byte address of a pointer into a __shared__ object.
 __device__ __forceinline__ unsigned lds_addr(void* p) {
   return (unsigned)(uintptr_t)(lds_ptr_t)(p);
@@ -157,11 +155,15 @@ __device__ __forceinline__ unsigned lds_addr(void* p) {
 // filled gets a wait for ALL loads in flight, which drains the operand
 // pipeline each K step.  The order between these loads and the LDS reads of
 // their data is kept explicitly (CCE_WAIT_VMCNT, then a barrier).  s_nop
-// covers the M0 write-to-use hazard.
-__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, unsigned m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+// covers the M0 write-to-use hazard.  soff (wave-uniform, an SGPR) is added to
+// the address but takes no part in the buffer's range check, so it carries
+// only offsets that keep a valid row inside its row (the K offset of a slice):
+// the per-lane offsets then stay the same for every slice and stay in
+// registers across the loop.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, int voff, unsigned m0, int soff) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(m0)
+               : "v"(voff), "s"(rsrc), "s"(m0), "s"(soff)
                : "m0");
 }
 
@@ -260,14 +262,14 @@ struct DmaOperand {
   // forms, whether this lane's chunk is inside K.
   struct Slice {
     i32x4 rs;
-    int kb;  // bytes added to every offset
+    int kb;  // bytes added to every address (wave-uniform: the instruction's SGPR offset)
     bool kv;
   };
   __device__ __forceinline__ Slice slice(int k0) const {
     Slice sl;
     if (MODE == OP_ROW || MODE == OP_BLK) {
       sl.rs = rsrc;
-      sl.kb = MODE == OP_BLK ? k0 * 512 : k0 * 2;
+      sl.kb = __builtin_amdgcn_readfirstlane(MODE == OP_BLK ? k0 * 512 : k0 * 2);
       sl.kv = MODE == OP_BLK || !KTAIL || k0 + c8 < K;
     } else {
       const u16* sb;
@@ -292,10 +294,10 @@ struct DmaOperand {
   __device__ __forceinline__ void issue(const Slice& sl, unsigned dst, int p) const {
     int off;
     if (MODE == OP_ROW || MODE == OP_BLK)
-      off = sl.kv ? voff[0] + p * pstride + sl.kb : 0x7ffffff0;
+      off = sl.kv ? voff[0] + p * pstride : 0x7ffffff0;
     else
       off = voff[p & 1] + (p >> 1) * pstride;
-    dma16(sl.rs, off, dst + ldsw + p * 1024);
+    dma16(sl.rs, off, dst + ldsw + p * 1024, sl.kb);
   }
 
   // All 4 loads of K-slice k0.
@@ -571,6 +573,11 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
                                           const int* __restrict__ kflags, int kflag_stride,
                                           const unsigned char* ring, unsigned ring_lds,
                                           floatx16 (&acc)[4][4]) {
+  // The LDS stage addresses are ring_lds plus constants; redefining ring_lds
+  // (an empty asm) here and at every unrolled group keeps the compiler from
+  // hoisting all of them out of the loops into scalar registers, which pushes
+  // other values to scratch, whose reloads then wait for every load in flight.
+  asm volatile("" : "+s"(ring_lds));
   bool all_active = true;
   if (SKIP) {
     // one pass over the tile's K-block flags (lanes stride over the blocks),
@@ -622,6 +629,7 @@ __device__ __forceinline__ void gemm_loop(const DmaOperand<AMODE, KTAIL>& da,
     return;
   }
   for (int kt0 = 0; kt0 < nk; kt0 += NSTAGE) {
+    asm volatile("" : "+s"(ring_lds));
 #pragma unroll
     for (int j = 0; j < NSTAGE; ++j) {
       const int kt = kt0 + j;

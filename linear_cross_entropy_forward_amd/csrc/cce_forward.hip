@@ -87,15 +87,20 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
     m_run[jj] = NEG_INF;
     s_run[jj] = 0.f;
   }
-  const u16* Hb = H + (size_t)mt * TILE * D;
-  const int hrows = min(TILE, M - mt * TILE);
   const int t_end = min(t0 + (split + 1) * T, t1);
 
   for (int t = t0 + split * T; t < t_end; ++t) {
+    // per-tile operand descriptors are rebuilt from scalars every tile (the
+    // empty asm keeps them from being hoisted out of the loop and spilled:
+    // a scratch reload in the prologue would wait for every load in flight)
+    int mt_ = mt, D_ = D;
+    asm volatile("" : "+s"(mt_), "+s"(D_));
+    const u16* Hb = H + (size_t)mt_ * TILE * D_;
+    const int hrows = min(TILE, M - mt_ * TILE);
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D, D, min(TILE, V - v0), D},
-                                 OpRef{Hb, D, hrows, D}, D, nullptr, 0, sm, acc);
+    gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_},
+                                 OpRef{Hb, D_, hrows, D_}, D_, nullptr, 0, sm, acc);
     if (CAP) {
       const float k2 = 2.f * LOG2E / softcap;
 #pragma unroll
