@@ -34,8 +34,11 @@
 namespace cce {
 
 // The gradient entries of one recomputed tile, straight from the accumulators
-// to G: per (ii, jj, q) a lane holds 4 consecutive vocab entries of one token,
-// 8 bytes of one row of the block (vocab block wi*4 + ii of the tile).  !CAP:
+// to G: per (ii, jj, q) a lane holds 4 consecutive vocab entries of one token
+// (vocab block wi*4 + ii of the tile, entries 8q + 4*half .. +3 of the row); the
+// lanes l and l + 32 of a token trade halves with v_permlane32_swap so that
+// each stores 8 consecutive entries (16 bytes): lane l those of q = 0 and 2,
+// lane l + 32 those of q = 1 and 3.  !CAP:
 // acc holds the raw logits and the softmax entry exp(z - lse) is formed here;
 // CAP: acc holds t = tanh(z / c).  TGT: some token of this wave has its target
 // among the wave's vocab rows (else no entry is compared with the target);
@@ -50,7 +53,8 @@ __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[4][4],
   for (int jj = 0; jj < 4; ++jj) {
     const int tj = wj * 128 + jj * 32 + (lane & 31);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < 4; ++ii) {
+      unsigned pk[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float g[4];
@@ -70,9 +74,24 @@ __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[4][4],
           if (FILTER && p < filter_eps && !is_t) p = 0.f;
           g[e] = cf[jj] * (is_t ? p - 1.f : p) * sech2;
         }
-        *reinterpret_cast<u32x2*>(gt + (size_t)ii * 8192 + tj * 32 + 8 * q) =
-            u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+        pk[q][0] = pack_bf16x2(g[0], g[1]);
+        pk[q][1] = pack_bf16x2(g[2], g[3]);
       }
+#pragma unroll
+      for (int qp = 0; qp < 4; qp += 2) {
+        // lane l: its q = qp (entries 0..3) and lane l+32's (4..7); lane l+32:
+        // lane l's q = qp+1 (entries 8..11) and its own (12..15)
+        unsigned v[4];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto r = __builtin_amdgcn_permlane32_swap(pk[qp][d], pk[qp + 1][d], false, false);
+          v[d] = r[0];
+          v[2 + d] = r[1];
+        }
+        *reinterpret_cast<u32x4*>(gt + (size_t)ii * 8192 + tj * 32 + 8 * (qp + half)) =
+            u32x4{v[0], v[1], v[2], v[3]};
+      }
+    }
   }
 }
 
@@ -194,7 +213,7 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
   if (tid == 0) *flag = 1;
 
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
-  u16* gt = G + ((size_t)mt * nkbV + vt * 8 + wi * 4) * 8192 + 4 * half;
+  u16* gt = G + ((size_t)mt * nkbV + vt * 8 + wi * 4) * 8192;
 #define CCE_STORE(TGT, VT)                                                                  \
   store_grad_tile<CAP, FILTER, TGT, VT>(acc, nlse, cf, off, c1, filter_eps, vl0, vlen, half, wj, \
                                         lane, gt)
