@@ -284,6 +284,34 @@ __device__ __forceinline__ bool split_task(const GemmProb& p, int b, int& ta, in
   return true;
 }
 
+// 4x4 transpose inside each quad of lanes (lanes 4k .. 4k+3): lane x holds
+// column x of a 4x4 block (v[0..3] = rows 0..3); afterwards it holds row x
+// (v[0..3] = columns 0..3).  Two DPP stages: lanes x and x^2 trade a pair of
+// values, then lanes x and x^1 trade one value of each pair.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
+  const int x = lane & 3;
+  float t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = quad_perm<0x4E>(v[i]);  // lane x reads lane x^2
+  const bool lo = x < 2;
+  v[0] = lo ? v[0] : t[2];
+  v[1] = lo ? v[1] : t[3];
+  v[2] = lo ? t[0] : v[2];
+  v[3] = lo ? t[1] : v[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = quad_perm<0xB1>(v[i]);  // lane x reads lane x^1
+  const bool even = (x & 1) == 0;
+  v[0] = even ? v[0] : t[1];
+  v[1] = even ? t[0] : v[1];
+  v[2] = even ? v[2] : t[3];
+  v[3] = even ? t[2] : v[3];
+}
+
 // The dh and dW contractions of one vocab chunk in a single launch: workgroups
 // [0, p0.nl) take p0 (dh, the longer K), the rest take p1 (dW).  Dispatching
 // the long tiles first lets the short ones fill the tail, so the two problems
@@ -323,31 +351,53 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          Pt[(size_t)row * TILE + wj * 128 + jj * 32 + (lane & 31)] = acc[ii][jj][r];
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          float v[4] = {acc[ii][jj][4 * r4], acc[ii][jj][4 * r4 + 1], acc[ii][jj][4 * r4 + 2],
+                        acc[ii][jj][4 * r4 + 3]};
+          quad_transpose(v, lane);
+          const int row = wi * 128 + ii * 32 + 8 * r4 + 4 * half + (lane & 3);
+          const int col0 = wj * 128 + jj * 32 + (lane & 28);
+          *reinterpret_cast<float4*>(Pt + (size_t)row * TILE + col0) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
     return;
   }
+  // Each lane holds 4 consecutive rows of one column per (ii, r4, jj); a quad
+  // transpose gives it 4 consecutive columns of one row, stored (and for dh
+  // accumulated) as 16 bytes when C's rows are 16-byte aligned.
   float* const Cb = p.C;
+  const bool vec4 = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = ta * TILE + wi * 128 + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (row >= p.c_rows) continue;
-      float* crow = Cb + (size_t)row * p.ldc;
+    for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int col = tb * TILE + wj * 128 + jj * 32 + (lane & 31);
-        if (col < p.c_cols) {
-          if (accum) crow[col] += acc[ii][jj][r];
-          else crow[col] = acc[ii][jj][r];
+        float v[4] = {acc[ii][jj][4 * r4], acc[ii][jj][4 * r4 + 1], acc[ii][jj][4 * r4 + 2],
+                      acc[ii][jj][4 * r4 + 3]};
+        quad_transpose(v, lane);
+        const int row = ta * TILE + wi * 128 + ii * 32 + 8 * r4 + 4 * half + (lane & 3);
+        const int col0 = tb * TILE + wj * 128 + jj * 32 + (lane & 28);
+        if (row >= p.c_rows) continue;
+        float* const c = Cb + (size_t)row * p.ldc + col0;
+        if (vec4 && col0 + 4 <= p.c_cols) {
+          float4 o = make_float4(v[0], v[1], v[2], v[3]);
+          if (accum) {
+            const float4 q = *reinterpret_cast<const float4*>(c);
+            o.x += q.x;
+            o.y += q.y;
+            o.z += q.z;
+            o.w += q.w;
+          }
+          *reinterpret_cast<float4*>(c) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col0 + e < p.c_cols) c[e] = accum ? c[e] + v[e] : v[e];
         }
       }
-    }
 }
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
