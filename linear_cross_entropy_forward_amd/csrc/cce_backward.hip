@@ -43,17 +43,20 @@ namespace cce {
 // CAP: acc holds t = tanh(z / c).  TGT: some token of this wave has its target
 // among the wave's vocab rows (else no entry is compared with the target);
 // VT: the tile runs past the chunk's last vocab row (those entries are 0).
-template <bool CAP, bool FILTER, bool TGT, bool VT>
-__device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[4][4],
+// NI: vocab blocks of 32 in acc (4; 2 for the VGPR part of a tall tile); only
+// the first nblk of them are stored (the blocks the dh contraction reads).
+template <bool CAP, bool FILTER, bool TGT, bool VT, int NI = 4>
+__device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
                                                 const float (&nlse)[4], const float (&cf)[4],
                                                 const int (&off)[4], float c1, float filter_eps,
                                                 int vl0, int vlen, int half, int wj, int lane,
-                                                u16* __restrict__ gt) {
+                                                u16* __restrict__ gt, int nblk = NI) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int tj = wj * 128 + jj * 32 + (lane & 31);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < NI; ++ii) {
+      if (ii >= nblk) continue;
       unsigned pk[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -217,6 +220,78 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
 #define CCE_STORE(TGT, VT)                                                                  \
   store_grad_tile<CAP, FILTER, TGT, VT>(acc, nlse, cf, off, c1, filter_eps, vl0, vlen, half, wj, \
                                         lane, gt)
+  if (wave_has_tgt) {
+    if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
+  } else {
+    if (vtail) CCE_STORE(false, true); else CCE_STORE(false, false);
+  }
+#undef CCE_STORE
+}
+
+// The tall form of the recompute (384 vocab rows x 256 tokens per tile, the
+// forward's tall GEMM; fewer operand bytes per FLOP), used when the operands
+// allow it and no tile is skipped (block_eps = 0, so the dh / dW contractions
+// read no tile flags).  Wave wi holds vocab blocks 6 wi .. 6 wi + 5 of the
+// tile: 4 in acc.a, 2 in acc.v.  Blocks at or past nkb (the blocks the dh
+// contraction reads: the chunk rounded up to 256) are not stored; entries past
+// vlen within the stored blocks are 0.
+template <bool FILTER, bool CAP>
+__global__ __launch_bounds__(NT, 1) void k_recompute_tall(
+    const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
+    const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
+    int vlen, int nMt, int nvt, float softcap, float filter_eps, u16* __restrict__ G, int nkbV,
+    int nkb) {
+  __shared__ SmemTall sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+  int mt, vt;
+  if (!map_tile(blockIdx.x, gridDim.x, nMt, nvt, 8, mt, vt)) return;
+
+  AccTall acc;
+  gemm_tile_tall(OpRef{Wc + (size_t)vt * TALL * D, D, min(TALL, vlen - vt * TALL), D},
+                 OpRef{H + (size_t)mt * TILE * D, D, min(TILE, M - mt * TILE), D}, D, sm, acc);
+
+  const int vl0 = vt * TALL + wi * 192;  // chunk-local vocab row of this wave's first A row
+  float nlse[4], cf[4];
+  int off[4], off2[4];
+  bool any_tgt_lane = false;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
+    const bool ok = j < M;
+    nlse[jj] = ok ? -lse[j] * LOG2E : NEG_INF;  // padding rows: no softmax entries
+    cf[jj] = ok ? coef[j] : 0.f;
+    const int yy = ok ? y[j] : -1;
+    off[jj] = (yy >= 0) ? yy - (v0 + vl0) - 4 * half : -1000000;
+    off2[jj] = off[jj] - 128;
+    const int o = (yy >= 0) ? yy - (v0 + vl0) : -1;
+    any_tgt_lane |= (unsigned)o < 192u;
+  }
+  const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
+  if (CAP) {
+    const float k2 = 2.f * LOG2E / softcap;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc.a[ii][jj][r] = tanh_scaled(acc.a[ii][jj][r], k2);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) acc.v[ii][jj][r] = tanh_scaled(acc.v[ii][jj][r], k2);
+      }
+  }
+  const bool vtail = vt * TALL + TALL > vlen;
+  const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
+  const int b0 = vt * 12 + wi * 6;  // this wave's first vocab block of the chunk
+  const int nb = min(max(nkb - b0, 0), 6);
+  u16* gt = G + ((size_t)mt * nkbV + b0) * 8192;
+#define CCE_STORE(TGT, VT)                                                                     \
+  do {                                                                                         \
+    store_grad_tile<CAP, FILTER, TGT, VT, 4>(acc.a, nlse, cf, off, c1, filter_eps, vl0, vlen,  \
+                                             half, wj, lane, gt, min(nb, 4));                  \
+    store_grad_tile<CAP, FILTER, TGT, VT, 2>(acc.v, nlse, cf, off2, c1, filter_eps, vl0 + 128, \
+                                             vlen, half, wj, lane, gt + 4 * 8192, nb - 4);     \
+  } while (0)
   if (wave_has_tgt) {
     if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
   } else {
@@ -512,7 +587,26 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       Wc = a.Wbuf;
     }
     // 1. recompute + gradient tile
-    {
+#ifdef CCE_NO_TALL
+    const bool tall = false;
+#else
+    const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
+#endif
+    if (tall) {
+      const int nvt3 = (vlen + TALL - 1) / TALL;
+      const int n = pad8(a.nMt * nvt3);
+#define CCE_RECOMPUTE_T(FILT, CAP)                                                                 \
+  hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y, a.lse, \
+                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt3, a.softcap, a.filter_eps, a.G, nkbV,  \
+                     nvt * 8)
+      if (a.softcap > 0.f) {
+        if (filt) CCE_RECOMPUTE_T(true, true); else CCE_RECOMPUTE_T(false, true);
+      } else {
+        if (filt) CCE_RECOMPUTE_T(true, false); else CCE_RECOMPUTE_T(false, false);
+      }
+#undef CCE_RECOMPUTE_T
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
       const int n = pad8(a.nMt * nvt);
 #define CCE_RECOMPUTE(VEC, FILT, KT, CAP)                                                          \
   hipLaunchKernelGGL((k_recompute<VEC, FILT, KT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y,    \

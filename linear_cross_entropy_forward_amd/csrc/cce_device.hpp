@@ -210,7 +210,11 @@ struct OpRef {
 // Loads past a buffer resource's end read zero; an invalid chunk is pointed
 // past the end.  K forms rebase their resource every slice so that no offset
 // exceeds 32 bits whatever the matrix size.
-template <int MODE, bool KTAIL>
+//
+// NRW (row forms only): operand rows per wave, 64 (a 256-row tile) or 96 (the
+// 384-row A operand of the tall tile below); wave w then fills rows
+// NRW w .. NRW w + NRW - 1 with NRW / 16 instructions.
+template <int MODE, bool KTAIL, int NRW = 64>
 struct DmaOperand {
   i32x4 rsrc;  // row forms: over the whole tile
   const u16* base;
@@ -226,11 +230,11 @@ struct DmaOperand {
     ld = op.ld;
     rows = op.rows;
     K = K_;
-    ldsw = (unsigned)__builtin_amdgcn_readfirstlane(w * 4096);
+    ldsw = (unsigned)__builtin_amdgcn_readfirstlane(w * NRW * 64);
     if (MODE == OP_ROW || MODE == OP_BLK) {
       // row bits 0..3 are lane bits 2..5, so swz(row) = swz(lane >> 2) for every instruction
       const int c = (lane & 3) ^ swz(lane >> 2);
-      const int row0 = 64 * w + (lane >> 2);
+      const int row0 = NRW * w + (lane >> 2);
       if (MODE == OP_BLK) {
         rsrc = make_rsrc(op.p, (unsigned)(K_ >> 5) * 16384u);
         voff[0] = row0 * 64 + c * 16;
@@ -300,11 +304,11 @@ struct DmaOperand {
     dma16(sl.rs, off, dst + ldsw + p * 1024, sl.kb);
   }
 
-  // All 4 loads of K-slice k0.
+  // All loads of K-slice k0 (4, or NRW / 16 for a row form).
   __device__ __forceinline__ void issue_all(int k0, unsigned dst) const {
     const Slice sl = slice(k0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) issue(sl, dst, p);
+    for (int p = 0; p < NRW / 16; ++p) issue(sl, dst, p);
   }
 };
 
@@ -686,6 +690,187 @@ __device__ __forceinline__ void gemm_tile(const OpRef& A, const OpRef& B, int K,
     }
     __syncthreads();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tall tile: A 384 rows x B 256 rows, both row-major [i][k] with K % 32 == 0
+// (the forward and the recompute: A = vocabulary rows, B = token rows).
+//
+// The core loop above is bound by the operand stream through each CU (bytes
+// per MFMA), not by the MFMAs.  A 384 x 256 tile needs 40 KB per 32-wide
+// K-slice for 1.5x the MFMAs of a 256 x 256 tile (32 KB): 17 % fewer operand
+// bytes per FLOP.  Each wave owns 192 x 128 = 6 x 4 MFMA tiles, 384 fp32
+// accumulators a lane: A tiles 0..3 live in the 256 AGPRs (the compiler's
+// MFMA form) and A tiles 4..5 in 128 VGPRs, whose MFMAs are written as
+// assembly (the compiler picks one register file for all of its MFMAs).
+//
+// The compiler does not see inside that assembly, so the MFMA hazards that
+// concern it are covered by hand: the accumulators pass through an s_nop
+// statement that names them as operands after they are zeroed (VALU write ->
+// MFMA read of SrcC) and after the K loop (MFMA write -> VALU read; 8-pass
+// MFMA: 11 wait states, 24 given).  Within the loop an accumulator is only
+// touched by its own MFMA, 24 MFMAs apart, and the A / B fragments are written
+// by LDS reads only, which the compiler's waitcnt insertion orders before the
+// MFMAs that read them.
+//
+// LDS: 4 stages of 40 KB (A 24 KB then B 16 KB), the whole 160 KB; the
+// layouts, the swizzle and the order of the K step are those of the core loop,
+// with 6 A fragment reads and 6 A loads per sub-step.
+// ---------------------------------------------------------------------------
+constexpr int TALL = 384;
+constexpr int TALL_A_BYTES = TALL * BK * 2;            // 24 KB
+constexpr int TALL_STAGE = TALL_A_BYTES + HALF_BYTES;  // 40 KB
+
+struct __align__(16) SmemTall {
+  unsigned char raw[NSTAGE * TALL_STAGE];
+};
+
+struct AccTall {
+  floatx16 a[4][4];  // A tiles 0..3 of the wave (AGPRs)
+  floatx16 v[2][4];  // A tiles 4..5 (VGPRs)
+};
+
+struct FragsTall {
+  bf16x8 a[6], b[4];
+};
+
+// acc += a . b^T on one 32x32x16 MFMA with the accumulator in VGPRs.
+__device__ __forceinline__ void mfma_vgpr(floatx16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+
+// The VGPR accumulators pass through NOPS wait states here: every access
+// before the statement completes before every access after it.
+#define CCE_TALL_FENCE(A, NOPS)                                                               \
+  asm volatile(NOPS                                                                            \
+               : "+v"((A).v[0][0]), "+v"((A).v[0][1]), "+v"((A).v[0][2]), "+v"((A).v[0][3]), \
+                 "+v"((A).v[1][0]), "+v"((A).v[1][1]), "+v"((A).v[1][2]), "+v"((A).v[1][3]))
+
+__device__ __forceinline__ void tall_zero(AccTall& A) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A.a[i][j][r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) A.v[i][j][r] = 0.f;
+    }
+  CCE_TALL_FENCE(A, "s_nop 4");
+}
+
+// After the last MFMA of a tile, before any other instruction reads the VGPR
+// accumulators.
+__device__ __forceinline__ void tall_drain(AccTall& A) {
+  CCE_TALL_FENCE(A, "s_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
+
+// Per-lane fragment offsets in a tall stage (row forms; see FragAddr).
+struct FragAddrTall {
+  int a, b, k0, k1;
+  __device__ __forceinline__ void init(int lane, int wi, int wj) {
+    const int r = lane & 31, half = lane >> 5;
+    const int sw = swz(r);  // rows r + 32 i + 192 wi (A) and r + 32 j + 128 wj (B)
+    k0 = (half ^ sw) << 4;
+    k1 = ((2 + half) ^ sw) << 4;
+    a = (wi * 192 + r) * 64;
+    b = TALL_A_BYTES + (wj * 128 + r) * 64;
+  }
+};
+
+// Fragment r (0..9) of a sub-step in the order the next sub-step's MFMAs
+// consume them: A0, B0, B1, B2, B3, A1, A2, A3, A4, A5.
+__device__ __forceinline__ void tall_read_frag(const unsigned char* stage, const FragAddrTall& fa,
+                                               int sub, int r, FragsTall& f) {
+  const int kc = sub ? fa.k1 : fa.k0;
+  if (r == 0) f.a[0] = *reinterpret_cast<const bf16x8*>(stage + fa.a + kc);
+  else if (r < 5) f.b[r - 1] = *reinterpret_cast<const bf16x8*>(stage + fa.b + (r - 1) * 2048 + kc);
+  else f.a[r - 4] = *reinterpret_cast<const bf16x8*>(stage + fa.a + (r - 4) * 2048 + kc);
+}
+
+__device__ __forceinline__ void tall_mfma(const FragsTall& f, int q, AccTall& acc) {
+  const int i = q >> 2, j = q & 3;
+  if (i < 4) acc.a[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.a[i][j], 0, 0, 0);
+  else mfma_vgpr(acc.v[i - 4][j], f.a[i], f.b[j]);
+}
+
+// One K step (slice kt in `cur`, kt+1 in `nxt`, kt+3 loaded into `far`):
+//   sub-step 0: 24 MFMAs; after even q < 20 one fragment read of sub-step 1,
+//     after q = 3, 7, .., 23 one of the 6 A loads of slice kt+3
+//   wait for this wave's loads of slice kt+1 (in flight may be slice kt+2's 10
+//   and the 6 just issued), barrier
+//   sub-step 1: 24 MFMAs; after even q < 20 one read of slice kt+1's first
+//     fragments, after q = 5, 11, 17, 23 one of the 4 B loads of slice kt+3.
+__device__ __forceinline__ void tall_step(const DmaOperand<OP_ROW, false, 96>& da,
+                                          const DmaOperand<OP_ROW, false, 64>& db,
+                                          const FragAddrTall& fa, int kn, const unsigned char* cur,
+                                          const unsigned char* nxt, unsigned far, FragsTall& f0,
+                                          FragsTall& f1, AccTall& acc) {
+  const DmaOperand<OP_ROW, false, 96>::Slice sa = da.slice(kn);
+#pragma unroll
+  for (int q = 0; q < 24; ++q) {
+    tall_mfma(f0, q, acc);
+    if ((q & 1) == 0 && q < 20) tall_read_frag(cur, fa, 1, q >> 1, f1);
+    else if ((q & 3) == 3) da.issue(sa, far, q >> 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slice kt+2 and the A half of kt+3 may be in flight)
+  ring_barrier();
+  const DmaOperand<OP_ROW, false, 64>::Slice sb = db.slice(kn);
+#pragma unroll
+  for (int q = 0; q < 24; ++q) {
+    tall_mfma(f1, q, acc);
+    if ((q & 1) == 0 && q < 20) tall_read_frag(nxt, fa, 0, q >> 1, f0);
+    else if (q % 6 == 5) db.issue(sb, far + TALL_A_BYTES, q / 6);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// acc = A[0:384, 0:K] . B[0:256, 0:K]^T, K % 32 == 0, both operands 16-byte
+// aligned row-major (rows past A.rows / B.rows read as zero).  Ends with every
+// load drained, a barrier (LDS free) and the VGPR accumulators readable.
+__device__ __forceinline__ void gemm_tile_tall(const OpRef& A, const OpRef& B, int K, SmemTall& sm,
+                                               AccTall& acc) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  tall_zero(acc);
+  FragAddrTall fa;
+  fa.init(lane, w & 1, w >> 1);
+  unsigned char* ring = sm.raw;
+  unsigned ring_lds = lds_addr(ring);
+  const int nk = K / BK;
+  DmaOperand<OP_ROW, false, 96> da;
+  DmaOperand<OP_ROW, false, 64> db;
+  da.init(A, K, lane, w);
+  db.init(B, K, lane, w);
+  asm volatile("" : "+s"(ring_lds));
+  const int klast = (nk - 1) * BK;
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) {
+    const int k = min(s * BK, klast);
+    da.issue_all(k, ring_lds + s * TALL_STAGE);
+    db.issue_all(k, ring_lds + s * TALL_STAGE + TALL_A_BYTES);
+  }
+  CCE_WAIT_VMCNT(20);  // slice 0 landed (slices 1 and 2 may be in flight)
+  ring_barrier();
+  FragsTall f0, f1;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) tall_read_frag(ring, fa, 0, r, f0);
+  for (int kt0 = 0; kt0 < nk; kt0 += NSTAGE) {
+    asm volatile("" : "+s"(ring_lds));
+#pragma unroll
+    for (int j = 0; j < NSTAGE; ++j) {
+      const int kt = kt0 + j;
+      if (kt < nk)
+        tall_step(da, db, fa, min((kt + 3) * BK, klast), ring + j * TALL_STAGE,
+                  ring + ((j + 1) & 3) * TALL_STAGE, ring_lds + ((j + 3) & 3) * TALL_STAGE, f0, f1,
+                  acc);
+    }
+  }
+  CCE_WAIT_VMCNT(0);
+  __syncthreads();
+  tall_drain(acc);
 }
 
 }  // namespace cce

@@ -163,6 +163,121 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
   }
 }
 
+// The tall form of the forward (384 vocab rows x 256 tokens per tile; fewer
+// operand bytes per FLOP, otherwise the same algorithm as k_fwd): used when
+// the operands allow it (16-byte aligned, D % 32 == 0) and no block maximum is
+// saved (that is kept per 256-entry block).  The last tile may run past V: its
+// entries with v >= V take no part, so no second launch is needed.
+__device__ __forceinline__ float tall_at(const AccTall& A, int ii, int jj, int r) {
+  return ii < 4 ? A.a[ii][jj][r] : A.v[ii - 4][jj][r];
+}
+
+template <bool TAIL>
+__device__ __forceinline__ void fwd_tall_update(const AccTall& acc, int vw, int V, int half,
+                                                float (&m_run)[4], float (&s_run)[4]) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float mx = NEG_INF;
+#pragma unroll
+    for (int ii = 0; ii < 6; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
+        if (ok) mx = fmaxf(mx, tall_at(acc, ii, jj, r));
+      }
+    const float mn = fmaxf(m_run[jj], mx);
+    if (TAIL && mn == NEG_INF) continue;  // no valid entry yet for this lane
+    const float nb = -mn * LOG2E;
+    float sum = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 6; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(tall_at(acc, ii, jj, r), LOG2E, nb));
+        if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
+      }
+    s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
+    m_run[jj] = mn;
+  }
+}
+
+// Workgroup (mt, split) runs tall vocab tiles [split*T, min((split+1)*T, nVt))
+// and writes partial slot `split`.
+template <bool CAP>
+__global__ __launch_bounds__(NT, 1) void k_fwd_tall(const u16* __restrict__ H,
+                                                    const u16* __restrict__ W, int M, int V, int D,
+                                                    int nMt, int S, int T, int nVt, int nlaunch,
+                                                    float softcap, float* __restrict__ part_m,
+                                                    float* __restrict__ part_s, int Mpad) {
+  __shared__ SmemTall sm;
+  int mt, split;
+  if (!map_tile(blockIdx.x, nlaunch, nMt, S, 8, mt, split)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+
+  float m_run[4], s_run[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    m_run[jj] = NEG_INF;
+    s_run[jj] = 0.f;
+  }
+  const int t_end = min((split + 1) * T, nVt);
+  for (int t = split * T; t < t_end; ++t) {
+    // per-tile descriptors from scalars every tile (not hoisted and spilled)
+    int mt_ = mt, D_ = D;
+    asm volatile("" : "+s"(mt_), "+s"(D_));
+    const u16* Hb = H + (size_t)mt_ * TILE * D_;
+    const int hrows = min(TILE, M - mt_ * TILE);
+    const int v0 = t * TALL;
+    AccTall acc;
+    gemm_tile_tall(OpRef{W + (size_t)v0 * D_, D_, min(TALL, V - v0), D_},
+                   OpRef{Hb, D_, hrows, D_}, D_, sm, acc);
+    if (CAP) {
+      const float k2 = 2.f * LOG2E / softcap;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc.a[ii][jj][r] = softcap * tanh_scaled(acc.a[ii][jj][r], k2);
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii) acc.v[ii][jj][r] = softcap * tanh_scaled(acc.v[ii][jj][r], k2);
+        }
+    }
+    if (v0 + TALL > V) fwd_tall_update<true>(acc, v0 + wi * 192, V, half, m_run, s_run);
+    else fwd_tall_update<false>(acc, v0 + wi * 192, V, half, m_run, s_run);
+  }
+
+  // lanes l and l^32 hold the same token; so do waves wi = 0 and wi = 1
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float mo = __shfl_xor(m_run[jj], 32);
+    const float so = __shfl_xor(s_run[jj], 32);
+    lse_merge(m_run[jj], s_run[jj], mo, so);
+  }
+  float* xm = reinterpret_cast<float*>(&sm);
+  float* xs = xm + 256;
+  __syncthreads();
+  if (wi == 1 && half == 0) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      xm[wj * 128 + jj * 32 + lane] = m_run[jj];
+      xs[wj * 128 + jj * 32 + lane] = s_run[jj];
+    }
+  }
+  __syncthreads();
+  if (wi == 0 && half == 0) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float m = m_run[jj], s = s_run[jj];
+      lse_merge(m, s, xm[wj * 128 + jj * 32 + lane], xs[wj * 128 + jj * 32 + lane]);
+      const int j = mt * TILE + wj * 128 + jj * 32 + lane;
+      part_m[(size_t)split * Mpad + j] = m;
+      part_s[(size_t)split * Mpad + j] = s;
+    }
+  }
+}
+
 // tgt[i] = h_i . W_{y_i} (fp32 sum of exact bf16 products), one wave per row,
 // then capped like every other logit when softcap > 0.  Rows whose target is
 // outside [0, V) are skipped (the merge reports them).
@@ -253,7 +368,29 @@ void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {
   S = (nVt + T - 1) / T;
 }
 
+bool fwd_use_tall(const FwdArgs& a) {
+#ifdef CCE_NO_TALL
+  return false;
+#else
+  return a.vec && a.D % BK == 0 && a.bm == nullptr;
+#endif
+}
+
 hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {
+  if (fwd_use_tall(a)) {
+    const int nVt = (a.V + TALL - 1) / TALL;
+    int S, T;
+    fwd_split_tiles(a.nMt, nVt, S, T);
+    const int nl = (a.nMt * S + 7) / 8 * 8;
+    if (a.softcap > 0.f)
+      hipLaunchKernelGGL(k_fwd_tall<true>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D,
+                         a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad);
+    else
+      hipLaunchKernelGGL(k_fwd_tall<false>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D,
+                         a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad);
+    slots = S;
+    return hipGetLastError();
+  }
   const int full = a.V / TILE;  // full vocab tiles
   slots = 0;
   if (full > 0) {

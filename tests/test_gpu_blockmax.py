@@ -80,9 +80,14 @@ def test_forward_block_max(device, case):
     logp0, lse0 = head.forward(h, W, y, softcap=cap)
     torch.cuda.synchronize()
     assert head.read_status() == 0
-    # the block maximum changes nothing else
-    assert logp.cpu().numpy().tobytes() == logp0.cpu().numpy().tobytes()
-    assert lse.cpu().numpy().tobytes() == lse0.cpu().numpy().tobytes()
+    # the block maximum changes nothing else: the forward that saves it tiles
+    # the vocabulary by 256 and the one that does not by 384 where the operands
+    # allow (fewer operand bytes per FLOP), so the fp32 sums are the same terms
+    # in another order: a few fp32 ulps of lse apart
+    lse_a, lse_b = lse.cpu().numpy(), lse0.cpu().numpy()
+    np.testing.assert_allclose(lse_a, lse_b, rtol=4e-6, atol=0)
+    np.testing.assert_allclose(logp.cpu().numpy(), logp0.cpu().numpy(), rtol=0,
+                               atol=float(4e-6 * np.abs(lse_b).max()))
     ref = O.block_max(wl.h64(), wl.W64(), cap)
     check_block_max(bm.cpu().numpy(), ref, "block_max")
 
