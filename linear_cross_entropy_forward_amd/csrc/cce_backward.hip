@@ -572,13 +572,31 @@ DhSplit dh_split(int nMt, int nDt, int nvt, bool with_dw, int Mpad, long long ma
   return r;
 }
 
+// Vocabulary entries per backward step when the recompute runs tall tiles:
+// the chunk (Vc, the workspace width) is narrowed to a multiple of 768 (two
+// tall tiles, three 256-blocks) whose nMt x (width / 384) recompute tiles fill
+// whole rounds of kCUs workgroups, if one within 1/8 of Vc exists (e.g. 15360
+// at 32 or 64 token tiles: exactly 5 or 10 rounds, against 5.4 or 10.75 at
+// 16384); otherwise Vc.
+static int tall_chunk(int Vc, int nMt) {
+  for (int w = Vc / 768 * 768; w >= Vc - Vc / 8 && w >= 768; w -= 768)
+    if ((long long)nMt * (w / TALL) % kCUs == 0) return w;
+  return Vc;
+}
+
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   hipError_t e;
   const int nDt = a.Dpad / kTile;
   const int nkbV = a.Vc / 32;
   const bool filt = a.filter_eps > 0.f;
-  for (int v0 = 0; v0 < a.V; v0 += a.Vc) {
-    const int vlen = a.V - v0 < a.Vc ? a.V - v0 : a.Vc;
+#ifdef CCE_NO_TALL
+  const bool tall = false;
+#else
+  const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
+#endif
+  const int vstep = tall ? tall_chunk(a.Vc, a.nMt) : a.Vc;
+  for (int v0 = 0; v0 < a.V; v0 += vstep) {
+    const int vlen = a.V - v0 < vstep ? a.V - v0 : vstep;
     const int nvt = (vlen + kTile - 1) / kTile;
     const float* bmc = (a.bm && a.block_eps > 0.f) ? a.bm + (size_t)(v0 / kTile) * a.M : nullptr;
     const u16* Wc = a.q.Wq ? nullptr : a.W + (size_t)v0 * a.D;
@@ -587,11 +605,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       Wc = a.Wbuf;
     }
     // 1. recompute + gradient tile
-#ifdef CCE_NO_TALL
-    const bool tall = false;
-#else
-    const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
-#endif
     if (tall) {
       const int nvt3 = (vlen + TALL - 1) / TALL;
       const int n = pad8(a.nMt * nvt3);

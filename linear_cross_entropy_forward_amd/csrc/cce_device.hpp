@@ -746,15 +746,20 @@ __device__ __forceinline__ void mfma_vgpr(floatx16& c, const bf16x8& a, const bf
                : "+v"((A).v[0][0]), "+v"((A).v[0][1]), "+v"((A).v[0][2]), "+v"((A).v[0][3]), \
                  "+v"((A).v[1][0]), "+v"((A).v[1][1]), "+v"((A).v[1][2]), "+v"((A).v[1][3]))
 
+// The zero comes from an assembly statement, so the compiler cannot keep a
+// zero vector across the tile loop (it would spill it, and the reload before
+// the first MFMA would wait for every operand load in flight).
 __device__ __forceinline__ void tall_zero(AccTall& A) {
+  float z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A.a[i][j][r] = 0.f;
+      for (int i = 0; i < 4; ++i) A.a[i][j][r] = z;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) A.v[i][j][r] = 0.f;
+      for (int i = 0; i < 2; ++i) A.v[i][j][r] = z;
     }
   CCE_TALL_FENCE(A, "s_nop 4");
 }

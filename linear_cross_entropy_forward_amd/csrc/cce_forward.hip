@@ -168,37 +168,98 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
 // the operands allow it (16-byte aligned, D % 32 == 0) and no block maximum is
 // saved (that is kept per 256-entry block).  The last tile may run past V: its
 // entries with v >= V take no part, so no second launch is needed.
-__device__ __forceinline__ float tall_at(const AccTall& A, int ii, int jj, int r) {
-  return ii < 4 ? A.a[ii][jj][r] : A.v[ii - 4][jj][r];
-}
-
-template <bool TAIL>
-__device__ __forceinline__ void fwd_tall_update(const AccTall& acc, int vw, int V, int half,
-                                                float (&m_run)[4], float (&s_run)[4]) {
+// Online update of the running (m, s) of the 4 tokens of this lane with the
+// NI x 16 entries per token of acc (vocab rows vw + ii*32 + ...); TAIL: rows
+// >= V take no part.
+template <int NI, bool TAIL>
+__device__ __forceinline__ void fwd_rows_update(const floatx16 (&acc)[NI][4], int vw, int V,
+                                                int half, float (&m_run)[4], float (&s_run)[4]) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float mx = NEG_INF;
 #pragma unroll
-    for (int ii = 0; ii < 6; ++ii)
+    for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
-        if (ok) mx = fmaxf(mx, tall_at(acc, ii, jj, r));
+        if (ok) mx = fmaxf(mx, acc[ii][jj][r]);
       }
     const float mn = fmaxf(m_run[jj], mx);
     if (TAIL && mn == NEG_INF) continue;  // no valid entry yet for this lane
     const float nb = -mn * LOG2E;
     float sum = 0.f;
 #pragma unroll
-    for (int ii = 0; ii < 6; ++ii)
+    for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(tall_at(acc, ii, jj, r), LOG2E, nb));
+        const float e = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nb));
+        if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
+      }
+    s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
+    m_run[jj] = mn;
+    // one token at a time: the scheduler may not interleave the tokens' exps
+    // (that raises the register demand past what the accumulators leave)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Online update with the VGPR part of a tall tile (vocab rows vw .. vw + 63 of
+// the wave), read back from LDS where fwd_tall_stash left it: per token, its
+// 32 entries, then the same max / sum-exp fold as fwd_rows_update.
+template <bool TAIL>
+__device__ __forceinline__ void fwd_stash_update(const unsigned char* st, int lane, int vw, int V,
+                                                 int half, float (&m_run)[4], float (&s_run)[4]) {
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float x[2][16];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 q = *reinterpret_cast<const float4*>(st + (((ii * 4 + jj) * 4 + r4) * 64 + lane) * 16);
+        x[ii][4 * r4] = q.x;
+        x[ii][4 * r4 + 1] = q.y;
+        x[ii][4 * r4 + 2] = q.z;
+        x[ii][4 * r4 + 3] = q.w;
+      }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
+        if (ok) mx = fmaxf(mx, x[ii][r]);
+      }
+    const float mn = fmaxf(m_run[jj], mx);
+    if (TAIL && mn == NEG_INF) continue;
+    const float nb = -mn * LOG2E;
+    float sum = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(x[ii][r], LOG2E, nb));
         if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
       }
     s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
     m_run[jj] = mn;
   }
+}
+
+// The VGPR part of a tall tile (8 MFMA tiles, 128 values a lane) into this
+// wave's 32 KB of the drained operand ring, as float4 pieces ordered
+// [tile][r/4][lane] (consecutive lanes, consecutive 16 bytes): the registers
+// are then free before the epilogue reads the AGPR part.
+__device__ __forceinline__ void fwd_tall_stash(const AccTall& acc, unsigned char* st, int lane) {
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(st + (((ii * 4 + jj) * 4 + r4) * 64 + lane) * 16) =
+            make_float4(acc.v[ii][jj][4 * r4], acc.v[ii][jj][4 * r4 + 1], acc.v[ii][jj][4 * r4 + 2],
+                        acc.v[ii][jj][4 * r4 + 3]);
 }
 
 // Workgroup (mt, split) runs tall vocab tiles [split*T, min((split+1)*T, nVt))
@@ -244,8 +305,19 @@ __global__ __launch_bounds__(NT, 1) void k_fwd_tall(const u16* __restrict__ H,
           for (int ii = 0; ii < 2; ++ii) acc.v[ii][jj][r] = softcap * tanh_scaled(acc.v[ii][jj][r], k2);
         }
     }
-    if (v0 + TALL > V) fwd_tall_update<true>(acc, v0 + wi * 192, V, half, m_run, s_run);
-    else fwd_tall_update<false>(acc, v0 + wi * 192, V, half, m_run, s_run);
+    // the ring is drained (gemm_tile_tall ended with a barrier); each wave
+    // parks its VGPR part in its own 32 KB and reads it back itself
+    unsigned char* st = sm.raw + w * 32768;
+    fwd_tall_stash(acc, st, lane);
+    const int vw = v0 + wi * 192;
+    if (v0 + TALL > V) {
+      fwd_rows_update<4, true>(acc.a, vw, V, half, m_run, s_run);
+      fwd_stash_update<true>(st, lane, vw + 128, V, half, m_run, s_run);
+    } else {
+      fwd_rows_update<4, false>(acc.a, vw, V, half, m_run, s_run);
+      fwd_stash_update<false>(st, lane, vw + 128, V, half, m_run, s_run);
+    }
+    __syncthreads();  // every wave's stash read before the next tile's loads fill the ring
   }
 
   // lanes l and l^32 hold the same token; so do waves wi = 0 and wi = 1
