@@ -72,7 +72,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, workload: str):
     res = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         d = per_dispatch(path, counter)
-        fwd = [v for (i, n), v in d.items() if "k_fwd<" in n]
+        fwd = [v for (i, n), v in d.items() if "k_fwd<" in n or "k_fwd_tall<" in n]
+        kname = "k_fwd_tall" if any("k_fwd_tall<" in n for (i, n) in d) else "k_fwd"
         copy = [v for (i, n), v in d.items() if "copyBuffer" in n or "copy" in n.lower()]
         copy = [v for v in copy if v > 1e5]          # the 1 GiB copy, not small transfers
         if not fwd or not copy:
@@ -80,7 +81,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, workload: str):
         scale = (1 << 30) / (max(copy) * 1024.0)      # true bytes per counted byte
         res[counter] = {"kib_per_launch": sum(fwd) / len(fwd), "copy_kib": max(copy),
                         "scale": scale, "bytes_per_launch": sum(fwd) / len(fwd) * 1024.0 * scale}
-    out = {"workload": workload, "kernel": "k_fwd", "kernel_source_hash": B.kernel_source_hash(),
+    out = {"workload": workload, "kernel": kname, "kernel_source_hash": B.kernel_source_hash(),
            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
            "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
     with open(out_json, "w") as f:
@@ -289,6 +290,11 @@ def main():
     fwd_flops = 2.0 * wl.M * wl.V * wl.D
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tflops = (n_contr - 1) * fwd_flops / (bwd_ms * 1e-3) / 1e12
+    # the forward runs 384 x 256 tiles (k_fwd_tall) when D % 32 == 0 and no block
+    # maximum is saved, else 256 x 256 tiles (k_fwd); the recompute likewise
+    # (k_recompute_tall) when no tile is skipped
+    fwd_kernel = "k_fwd_tall" if (wl.D % 32 == 0 and not args.block_max) else "k_fwd"
+    rec_kernel = "k_recompute_tall" if (wl.D % 32 == 0 and not feps > 0) else "k_recompute"
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
         try:
@@ -331,15 +337,15 @@ def main():
                      "backward": round(bwd_ms, 4)},
         "workspace_bytes": (B.workspace_bytes_q if quant else B.workspace_bytes)(wl.M, wl.V, wl.D),
         "device_status": status,
-        "roofline": {"kernel": "cce_forward_q (k_dequant + k_fwd per chunk)" if quant
-                     else "k_fwd (cce_forward)", "bound": "mfma",
+        "roofline": {"kernel": f"cce_forward_q (k_dequant + {fwd_kernel} per chunk)" if quant
+                     else f"{fwd_kernel} (cce_forward)", "bound": "mfma",
                      "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None if quant else traffic},
         # the backward's kernels (per vocab chunk: recompute, then dh + dW) timed
         # together live around cce_backward: 3 contractions of 2*M*V*D FLOPs
-        "roofline_backward": {"kernels": "k_dequant + k_recompute + k_grads (dh) (cce_backward_q)"
-                              if quant else "k_recompute + k_grads (cce_backward)",
+        "roofline_backward": {"kernels": f"k_dequant + {rec_kernel} + k_grads (dh) (cce_backward_q)"
+                              if quant else f"{rec_kernel} + k_grads (cce_backward)",
                               "bound": "mfma", "achieved": round(bwd_tflops, 2),
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},

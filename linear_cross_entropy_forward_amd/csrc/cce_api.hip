@@ -38,6 +38,7 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
   size_t part_m, part_s, tgt, pairs, g, flags;
+  size_t g2;  // the second gradient buffer of the pipelined backward (0: none)
   size_t psplit;  // split-K partial tiles of dh (psplit_tiles of 256 x 256 fp32)
   long long psplit_tiles;
   size_t total;
@@ -79,6 +80,9 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   const size_t base = off;
+  // the pipelined backward (tall recompute tiles, D % 32 == 0) alternates
+  // between two gradient buffers
+  L.g2 = D % 32 == 0 ? take((size_t)L.Mpad * L.Vc * 2) : 0;
   L.psplit_tiles = split_tiles(L, true);
   L.psplit = take((size_t)L.psplit_tiles * kTile * kTile * 4);
   L.total = off;
@@ -270,6 +274,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.dh = dh;
   a.dW = dW;
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
+  a.G2 = L.g2 ? reinterpret_cast<cce::u16*>(base + L.g2) : nullptr;
   a.flags = reinterpret_cast<int*>(base + L.flags);
   a.status = dev_status;
   a.bm = block_max;

@@ -45,12 +45,15 @@ namespace cce {
 // VT: the tile runs past the chunk's last vocab row (those entries are 0).
 // NI: vocab blocks of 32 in acc (4; 2 for the VGPR part of a tall tile); only
 // the first nblk of them are stored (the blocks the dh contraction reads).
-template <bool CAP, bool FILTER, bool TGT, bool VT, int NI = 4>
+// RAW (with CAP): acc holds the raw logits z and t = tanh(z / c) is formed here
+// (k2 = 2 log2(e) / c), so no pass rewrites the accumulators beforehand.
+template <bool CAP, bool FILTER, bool TGT, bool VT, int NI = 4, bool RAW = false>
 __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
                                                 const float (&nlse)[4], const float (&cf)[4],
                                                 const int (&off)[4], float c1, float filter_eps,
                                                 int vl0, int vlen, int half, int wj, int lane,
-                                                u16* __restrict__ gt, int nblk = NI) {
+                                                u16* __restrict__ gt, int nblk = NI,
+                                                float k2 = 0.f) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int tj = wj * 128 + jj * 32 + (lane & 31);
@@ -66,7 +69,7 @@ __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
           const bool vbad = VT && (vl0 + ii * 32 + 8 * q + 4 * half + e >= vlen);
           float p, sech2 = 1.f;
           if (CAP) {
-            const float t = acc[ii][jj][4 * q + e];
+            const float t = RAW ? tanh_scaled(acc[ii][jj][4 * q + e], k2) : acc[ii][jj][4 * q + e];
             p = vbad ? 0.f : fast_exp2(fmaf(t, c1, nlse[jj]));
             sech2 = 1.f - t * t;
           } else {
@@ -235,17 +238,35 @@ __global__ __launch_bounds__(NT, 1) void k_recompute(
 // tile: 4 in acc.a, 2 in acc.v.  Blocks at or past nkb (the blocks the dh
 // contraction reads: the chunk rounded up to 256) are not stored; entries past
 // vlen within the stored blocks are 0.
+struct RecArgs {
+  const u16* H;
+  const u16* Wc;  // the chunk's head rows
+  const int* y;
+  const float* lse;
+  const float* coef;
+  int M, D, v0, vlen, nMt, nvt;  // nvt: tall tiles of the chunk
+  float softcap, filter_eps;
+  u16* G;    // the chunk's gradient buffer (blocked)
+  int nkbV;  // 32-wide vocab blocks per token tile of G
+  int nkb;   // blocks the dh contraction reads
+  int nl;    // workgroups of the recompute (a multiple of 8)
+};
+
+// Recompute task b (of r.nl) of a chunk: one tall tile.
 template <bool FILTER, bool CAP>
-__global__ __launch_bounds__(NT, 1) void k_recompute_tall(
-    const u16* __restrict__ H, const u16* __restrict__ Wc, const int* __restrict__ y,
-    const float* __restrict__ lse, const float* __restrict__ coef, int M, int D, int v0,
-    int vlen, int nMt, int nvt, float softcap, float filter_eps, u16* __restrict__ G, int nkbV,
-    int nkb) {
-  __shared__ SmemTall sm;
+__device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, SmemTall& sm) {
+  const u16* __restrict__ H = r.H;
+  const u16* __restrict__ Wc = r.Wc;
+  const int* __restrict__ y = r.y;
+  const float* __restrict__ lse = r.lse;
+  const float* __restrict__ coef = r.coef;
+  const int M = r.M, D = r.D, v0 = r.v0, vlen = r.vlen, nkbV = r.nkbV, nkb = r.nkb;
+  const float softcap = r.softcap, filter_eps = r.filter_eps;
+  u16* __restrict__ G = r.G;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   int mt, vt;
-  if (!map_tile(blockIdx.x, gridDim.x, nMt, nvt, 8, mt, vt)) return;
+  if (!map_tile(b, r.nl, r.nMt, r.nvt, 8, mt, vt)) return;
 
   AccTall acc;
   gemm_tile_tall(OpRef{Wc + (size_t)vt * TALL * D, D, min(TALL, vlen - vt * TALL), D},
@@ -268,18 +289,7 @@ __global__ __launch_bounds__(NT, 1) void k_recompute_tall(
     any_tgt_lane |= (unsigned)o < 192u;
   }
   const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
-  if (CAP) {
-    const float k2 = 2.f * LOG2E / softcap;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) acc.a[ii][jj][r] = tanh_scaled(acc.a[ii][jj][r], k2);
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) acc.v[ii][jj][r] = tanh_scaled(acc.v[ii][jj][r], k2);
-      }
-  }
+  const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;  // the cap's tanh is taken at the store
   const bool vtail = vt * TALL + TALL > vlen;
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
   const int b0 = vt * 12 + wi * 6;  // this wave's first vocab block of the chunk
@@ -287,10 +297,11 @@ __global__ __launch_bounds__(NT, 1) void k_recompute_tall(
   u16* gt = G + ((size_t)mt * nkbV + b0) * 8192;
 #define CCE_STORE(TGT, VT)                                                                     \
   do {                                                                                         \
-    store_grad_tile<CAP, FILTER, TGT, VT, 4>(acc.a, nlse, cf, off, c1, filter_eps, vl0, vlen,  \
-                                             half, wj, lane, gt, min(nb, 4));                  \
-    store_grad_tile<CAP, FILTER, TGT, VT, 2>(acc.v, nlse, cf, off2, c1, filter_eps, vl0 + 128, \
-                                             vlen, half, wj, lane, gt + 4 * 8192, nb - 4);     \
+    store_grad_tile<CAP, FILTER, TGT, VT, 4, true>(acc.a, nlse, cf, off, c1, filter_eps, vl0,  \
+                                                   vlen, half, wj, lane, gt, min(nb, 4), k2);  \
+    store_grad_tile<CAP, FILTER, TGT, VT, 2, true>(acc.v, nlse, cf, off2, c1, filter_eps,      \
+                                                   vl0 + 128, vlen, half, wj, lane,            \
+                                                   gt + 4 * 8192, nb - 4, k2);                 \
   } while (0)
   if (wave_has_tgt) {
     if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
@@ -298,6 +309,12 @@ __global__ __launch_bounds__(NT, 1) void k_recompute_tall(
     if (vtail) CCE_STORE(false, true); else CCE_STORE(false, false);
   }
 #undef CCE_STORE
+}
+
+template <bool FILTER, bool CAP>
+__global__ __launch_bounds__(NT, 1) void k_recompute_tall(RecArgs r) {
+  __shared__ SmemTall sm;
+  recompute_tall_tile<FILTER, CAP>(r, blockIdx.x, sm);
 }
 
 // One fp32-output contraction C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k]
@@ -394,9 +411,8 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
 //   dh: A = G (blocked), B = W[chunk] read transposed (K = vocab)
 //   dW: A = G read transposed (K = tokens), B = h read transposed
 template <bool SKIP, bool VEC>
-__global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
-  __shared__ Smem sm;
-  int b = blockIdx.x;
+__device__ __forceinline__ void grads_task(const GemmProb& p0, const GemmProb& p1, int b,
+                                           Smem& sm) {
   const bool second = b >= p0.nl;
   const GemmProb p = second ? p1 : p0;
   if (second) b -= p0.nl;
@@ -473,6 +489,26 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
             if (col0 + e < p.c_cols) c[e] = accum ? c[e] + v[e] : v[e];
         }
       }
+}
+
+template <bool SKIP, bool VEC>
+__global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
+  __shared__ Smem sm;
+  grads_task<SKIP, VEC>(p0, p1, blockIdx.x, sm);
+}
+
+// One launch of the pipelined backward: the dh / dW tasks of vocab chunk c
+// (workgroups [0, p0.nl + p1.nl), reading chunk c's gradient buffer) and the
+// recompute tiles of chunk c + 1 (the rest, writing the other buffer).  The
+// long dh tasks go first, then dW, then the recompute tiles; the two kinds
+// fill each other's partial rounds, and the recompute's gradient stores
+// overlap other workgroups' contractions.
+template <bool FILTER, bool CAP>
+__global__ __launch_bounds__(NT, 1) void k_bwd_fused(GemmProb p0, GemmProb p1, RecArgs r) {
+  __shared__ SmemTall sm;
+  const int b = blockIdx.x, ng = p0.nl + p1.nl;
+  if (b < ng) grads_task<false, true>(p0, p1, b, *reinterpret_cast<Smem*>(&sm));
+  else recompute_tall_tile<FILTER, CAP>(r, b - ng, sm);
 }
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
@@ -584,19 +620,102 @@ static int tall_chunk(int Vc, int nMt) {
   return Vc;
 }
 
-hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
-  hipError_t e;
+// The dh / dW problems of one vocab chunk [v0, v0 + vlen) over the gradient
+// buffer G (see the kernels above for the operand forms).
+static void grads_probs(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* G, GemmProb& dh,
+                        GemmProb& dw, DhSplit& sp) {
   const int nDt = a.Dpad / kTile;
   const int nkbV = a.Vc / 32;
+  const int nvt = (vlen + kTile - 1) / kTile;
+  const int fstride = a.Vc / kTile;
+  const bool with_dw = a.q.Wq == nullptr;
+  sp = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.P_tiles);
+  const int nT = a.nMt * nDt;
+  const int dh_nl =
+      sp.ks == 1 ? pad8(nT) : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
+  dh = GemmProb{OpRef{G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
+                (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, dh_nl, a.flags,
+                fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P};
+  dw = GemmProb{OpRef{G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
+                (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
+                a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr};
+}
+
+static RecArgs rec_args(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* G) {
+  const int nvt3 = (vlen + TALL - 1) / TALL;
+  return RecArgs{a.H,     Wc,           a.y, a.lse, a.coef, a.M, a.D,        v0,
+                 vlen,    a.nMt,        nvt3, a.softcap, a.filter_eps, G, a.Vc / 32,
+                 (vlen + kTile - 1) / kTile * 8, pad8(a.nMt * nvt3)};
+}
+
+static hipError_t split_reduce(const GemmProb& dh, const DhSplit& sp, hipStream_t st) {
+  const int nT = dh.nA * dh.nB;
+  if (sp.n_full < nT)
+    hipLaunchKernelGGL(k_split_reduce, dim3(nT - sp.n_full, TILE / 16), dim3(256), 0, st, dh);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
+  hipError_t e;
+  const int nkbV = a.Vc / 32;
   const bool filt = a.filter_eps > 0.f;
+  const bool cap = a.softcap > 0.f;
 #ifdef CCE_NO_TALL
   const bool tall = false;
 #else
   const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
 #endif
   const int vstep = tall ? tall_chunk(a.Vc, a.nMt) : a.Vc;
-  for (int v0 = 0; v0 < a.V; v0 += vstep) {
-    const int vlen = a.V - v0 < vstep ? a.V - v0 : vstep;
+  // the vocabulary chunks; the last one takes whatever is left when it fits
+  // the workspace width (no short remainder chunk that runs the chip a
+  // fraction full)
+  std::vector<std::pair<int, int>> chunks;
+  for (int v0 = 0, vlen = 0; v0 < a.V; v0 += vlen) {
+    vlen = a.V - v0 <= a.Vc ? a.V - v0 : vstep;
+    chunks.emplace_back(v0, vlen);
+  }
+  const int nch = (int)chunks.size();
+
+  // Pipelined form (bf16 head, tall recompute, a second gradient buffer):
+  // recompute chunk 0, then one launch per chunk c running c's dh / dW tasks
+  // and c + 1's recompute tiles into the other buffer.  Stream order keeps
+  // every dependence: chunk c's buffer is complete before the launch that
+  // reads it, and is rewritten (by chunk c + 2's recompute) only in the launch
+  // after the one that read it; dh accumulates chunk by chunk as before.
+  if (tall && a.q.Wq == nullptr && a.G2 != nullptr) {
+    u16* const Gb[2] = {a.G, a.G2};
+    {
+      const RecArgs r = rec_args(a, 0, chunks[0].second, a.W, Gb[0]);
+#define CCE_REC(FILT, CAP) hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r)
+      if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
+      else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
+#undef CCE_REC
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    for (int c = 0; c < nch; ++c) {
+      const int v0 = chunks[c].first, vlen = chunks[c].second;
+      GemmProb dh, dw;
+      DhSplit sp;
+      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp);
+      if (c + 1 < nch) {
+        const int v1 = chunks[c + 1].first;
+        const RecArgs r = rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]);
+        const dim3 grid(dh.nl + dw.nl + r.nl);
+#define CCE_FUSED(FILT, CAP) hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r)
+        if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
+        else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
+#undef CCE_FUSED
+      } else {
+        hipLaunchKernelGGL((k_grads<false, true>), dim3(dh.nl + dw.nl), dim3(NT), 0, st, dh, dw);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+
+  for (int c = 0; c < nch; ++c) {
+    const int v0 = chunks[c].first, vlen = chunks[c].second;
     const int nvt = (vlen + kTile - 1) / kTile;
     const float* bmc = (a.bm && a.block_eps > 0.f) ? a.bm + (size_t)(v0 / kTile) * a.M : nullptr;
     const u16* Wc = a.q.Wq ? nullptr : a.W + (size_t)v0 * a.D;
@@ -606,18 +725,11 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     }
     // 1. recompute + gradient tile
     if (tall) {
-      const int nvt3 = (vlen + TALL - 1) / TALL;
-      const int n = pad8(a.nMt * nvt3);
-#define CCE_RECOMPUTE_T(FILT, CAP)                                                                 \
-  hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y, a.lse, \
-                     a.coef, a.M, a.D, v0, vlen, a.nMt, nvt3, a.softcap, a.filter_eps, a.G, nkbV,  \
-                     nvt * 8)
-      if (a.softcap > 0.f) {
-        if (filt) CCE_RECOMPUTE_T(true, true); else CCE_RECOMPUTE_T(false, true);
-      } else {
-        if (filt) CCE_RECOMPUTE_T(true, false); else CCE_RECOMPUTE_T(false, false);
-      }
-#undef CCE_RECOMPUTE_T
+      const RecArgs r = rec_args(a, v0, vlen, Wc, a.G);
+#define CCE_REC(FILT, CAP) hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r)
+      if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
+      else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
+#undef CCE_REC
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       const int n = pad8(a.nMt * nvt);
@@ -630,7 +742,6 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     if (filt) CCE_RECOMPUTE(VEC, true, KT, CAP); else CCE_RECOMPUTE(VEC, false, KT, CAP);          \
   } while (0)
       const bool kt = a.D % BK != 0;
-      const bool cap = a.softcap > 0.f;
       if (!a.vec) {
         if (cap) CCE_RECOMPUTE_F(false, false, true); else CCE_RECOMPUTE_F(false, false, false);
       } else if (kt) {
@@ -647,18 +758,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     //   dW: A = G^T (row tiles = chunk vocab tiles, K = Mpad), B = h^T, both read in place
     {
       const bool skip = a.block_eps > 0.f;
-      const int fstride = a.Vc / kTile;
       const bool with_dw = a.q.Wq == nullptr;
-      const DhSplit sp = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.P_tiles);
-      const int nT = a.nMt * nDt;
-      const int dh_nl = sp.ks == 1 ? pad8(nT)
-                                   : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
-      GemmProb dh{OpRef{a.G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
-                  (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, dh_nl, a.flags,
-                  fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P};
-      GemmProb dw{OpRef{a.G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
-                  (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
-                  a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr};
+      GemmProb dh, dw;
+      DhSplit sp;
+      grads_probs(a, v0, vlen, Wc, a.G, dh, dw, sp);
       // the quantised head is frozen: dh only
       const dim3 grid(with_dw ? dh.nl + dw.nl : dh.nl);
       if (a.vec) {
@@ -669,10 +772,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
         else hipLaunchKernelGGL((k_grads<false, false>), grid, dim3(NT), 0, st, dh, dw);
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (sp.n_full < nT) {
-        hipLaunchKernelGGL(k_split_reduce, dim3(nT - sp.n_full, TILE / 16), dim3(256), 0, st, dh);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-      }
+      if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
     }
   }
   return hipSuccess;

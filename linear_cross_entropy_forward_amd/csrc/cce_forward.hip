@@ -171,9 +171,13 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
 // Online update of the running (m, s) of the 4 tokens of this lane with the
 // NI x 16 entries per token of acc (vocab rows vw + ii*32 + ...); TAIL: rows
 // >= V take no part.
-template <int NI, bool TAIL>
+// CAP: acc holds raw logits and the entries are cap * tanh(z / cap) (k2 =
+// 2 log2(e) / cap); the cap is monotonic, so the largest entry is the cap of
+// the largest raw logit.
+template <int NI, bool TAIL, bool CAP>
 __device__ __forceinline__ void fwd_rows_update(const floatx16 (&acc)[NI][4], int vw, int V,
-                                                int half, float (&m_run)[4], float (&s_run)[4]) {
+                                                int half, float cap, float k2, float (&m_run)[4],
+                                                float (&s_run)[4]) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float mx = NEG_INF;
@@ -184,6 +188,7 @@ __device__ __forceinline__ void fwd_rows_update(const floatx16 (&acc)[NI][4], in
         const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
         if (ok) mx = fmaxf(mx, acc[ii][jj][r]);
       }
+    if (CAP && mx != NEG_INF) mx = cap * tanh_scaled(mx, k2);
     const float mn = fmaxf(m_run[jj], mx);
     if (TAIL && mn == NEG_INF) continue;  // no valid entry yet for this lane
     const float nb = -mn * LOG2E;
@@ -192,7 +197,8 @@ __device__ __forceinline__ void fwd_rows_update(const floatx16 (&acc)[NI][4], in
     for (int ii = 0; ii < NI; ++ii)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(acc[ii][jj][r], LOG2E, nb));
+        const float z = CAP ? cap * tanh_scaled(acc[ii][jj][r], k2) : acc[ii][jj][r];
+        const float e = fast_exp2(fmaf(z, LOG2E, nb));
         if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
       }
     s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
@@ -206,9 +212,10 @@ __device__ __forceinline__ void fwd_rows_update(const floatx16 (&acc)[NI][4], in
 // Online update with the VGPR part of a tall tile (vocab rows vw .. vw + 63 of
 // the wave), read back from LDS where fwd_tall_stash left it: per token, its
 // 32 entries, then the same max / sum-exp fold as fwd_rows_update.
-template <bool TAIL>
+template <bool TAIL, bool CAP>
 __device__ __forceinline__ void fwd_stash_update(const unsigned char* st, int lane, int vw, int V,
-                                                 int half, float (&m_run)[4], float (&s_run)[4]) {
+                                                 int half, float cap, float k2, float (&m_run)[4],
+                                                 float (&s_run)[4]) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     float x[2][16];
@@ -230,6 +237,7 @@ __device__ __forceinline__ void fwd_stash_update(const unsigned char* st, int la
         const bool ok = !TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V);
         if (ok) mx = fmaxf(mx, x[ii][r]);
       }
+    if (CAP && mx != NEG_INF) mx = cap * tanh_scaled(mx, k2);
     const float mn = fmaxf(m_run[jj], mx);
     if (TAIL && mn == NEG_INF) continue;
     const float nb = -mn * LOG2E;
@@ -238,7 +246,8 @@ __device__ __forceinline__ void fwd_stash_update(const unsigned char* st, int la
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(fmaf(x[ii][r], LOG2E, nb));
+        const float z = CAP ? cap * tanh_scaled(x[ii][r], k2) : x[ii][r];
+        const float e = fast_exp2(fmaf(z, LOG2E, nb));
         if (!TAIL || (vw + ii * 32 + 8 * (r >> 2) + 4 * half + (r & 3) < V)) sum += e;
       }
     s_run[jj] = s_run[jj] * fast_exp2((m_run[jj] - mn) * LOG2E) + sum;
@@ -293,29 +302,18 @@ __global__ __launch_bounds__(NT, 1) void k_fwd_tall(const u16* __restrict__ H,
     AccTall acc;
     gemm_tile_tall(OpRef{W + (size_t)v0 * D_, D_, min(TALL, V - v0), D_},
                    OpRef{Hb, D_, hrows, D_}, D_, sm, acc);
-    if (CAP) {
-      const float k2 = 2.f * LOG2E / softcap;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc.a[ii][jj][r] = softcap * tanh_scaled(acc.a[ii][jj][r], k2);
-#pragma unroll
-          for (int ii = 0; ii < 2; ++ii) acc.v[ii][jj][r] = softcap * tanh_scaled(acc.v[ii][jj][r], k2);
-        }
-    }
+    const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;  // the cap is taken in the update
     // the ring is drained (gemm_tile_tall ended with a barrier); each wave
     // parks its VGPR part in its own 32 KB and reads it back itself
     unsigned char* st = sm.raw + w * 32768;
     fwd_tall_stash(acc, st, lane);
     const int vw = v0 + wi * 192;
     if (v0 + TALL > V) {
-      fwd_rows_update<4, true>(acc.a, vw, V, half, m_run, s_run);
-      fwd_stash_update<true>(st, lane, vw + 128, V, half, m_run, s_run);
+      fwd_rows_update<4, true, CAP>(acc.a, vw, V, half, softcap, k2, m_run, s_run);
+      fwd_stash_update<true, CAP>(st, lane, vw + 128, V, half, softcap, k2, m_run, s_run);
     } else {
-      fwd_rows_update<4, false>(acc.a, vw, V, half, m_run, s_run);
-      fwd_stash_update<false>(st, lane, vw + 128, V, half, m_run, s_run);
+      fwd_rows_update<4, false, CAP>(acc.a, vw, V, half, softcap, k2, m_run, s_run);
+      fwd_stash_update<false, CAP>(st, lane, vw + 128, V, half, softcap, k2, m_run, s_run);
     }
     __syncthreads();  // every wave's stash read before the next tile's loads fill the ring
   }

@@ -105,6 +105,7 @@ struct BwdArgs {
   float* dh;
   float* dW;
   u16* G;      // [Mpad, Vc] bf16, blocked (256 x 32 blocks)
+  u16* G2;     // null, or a second such buffer (the pipelined backward)
   int* flags;  // [nMt, Vc / kTile]
   unsigned* status;
   // quantised head (q.Wq != null): each chunk is dequantised into Wbuf first,
