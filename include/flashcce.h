@@ -75,7 +75,9 @@ const char* cce_status_string(int status);
  * these sizes (one workspace serves all three).  Host-only; no GPU call.
  * It depends on M and D and is independent of V once V exceeds one backward
  * vocab chunk (16384 entries): the backward walks the vocabulary in chunks of
- * that fixed width.  Returns 0 for invalid sizes.
+ * at most that width, through a bf16 gradient buffer of Mpad x 16384 (two
+ * when D % 32 == 0: the backward then pipelines one chunk's contractions with
+ * the next chunk's recompute).  Returns 0 for invalid sizes.
  */
 size_t cce_workspace_bytes(int64_t M, int64_t V, int64_t D);
 
@@ -213,9 +215,11 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y,
  * cce_backward on the bf16-rounded dequantised head.
  */
 
-/* Workspace bytes for cce_forward_q / cce_backward_q: cce_workspace_bytes plus
- * one bf16 chunk of the dequantised head (16384 x D) and two [M] fp32 rows;
- * independent of V above one chunk.  0 for invalid sizes.  Host-only. */
+/* Workspace bytes for cce_forward_q / cce_backward_q: cce_workspace_bytes
+ * without its second gradient buffer (the quantised backward is not
+ * pipelined), plus one bf16 chunk of the dequantised head (16384 x D) and two
+ * [M] fp32 rows; independent of V above one chunk.  0 for invalid sizes.
+ * Host-only. */
 size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D);
 
 /* Forward over the quantised head; outputs as for cce_forward.  The running
