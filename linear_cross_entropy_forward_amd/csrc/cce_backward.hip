@@ -269,7 +269,7 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
   if (!map_tile(b, r.nl, r.nMt, r.nvt, 8, mt, vt)) return;
 
   AccTall acc;
-  gemm_tile_tall(OpRef{Wc + (size_t)vt * TALL * D, D, min(TALL, vlen - vt * TALL), D},
+  gemm_tile_tall<false>(OpRef{Wc + (size_t)vt * TALL * D, D, min(TALL, vlen - vt * TALL), D},
                  OpRef{H + (size_t)mt * TILE * D, D, min(TILE, M - mt * TILE), D}, D, sm, acc);
 
   const int vl0 = vt * TALL + wi * 192;  // chunk-local vocab row of this wave's first A row
@@ -342,6 +342,8 @@ struct GemmProb {
   int ks;      // K parts of a split tile (1: no split)
   int n_full;  // tiles (raster order) that are not split
   float* P;
+  int tall;    // the dW form in 384-row tiles (A = G^T over 12 vocab blocks; a.cols =
+               // the blocks' columns per token tile, a_tile = 12 blocks)
 };
 
 // Workgroup b of a problem -> (tile, K part, split-tile index u or -1); false
@@ -410,9 +412,50 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
 // together keep every CU busy (dh alone has too few output tiles).
 //   dh: A = G (blocked), B = W[chunk] read transposed (K = vocab)
 //   dW: A = G read transposed (K = tokens), B = h read transposed
+// dW of one tall tile (384 vocab rows x 256 columns of D): C rows ta*384 + ..,
+// written (dW is never accumulated).  The output leaves the accumulators
+// through the quad transpose, as 16-byte stores of 4 consecutive columns; the
+// VGPR part first, so its registers are free before the AGPR part is read.
+__device__ __forceinline__ void dw_tall_task(const GemmProb& p, int ta, int tb, const OpRef& bo,
+                                             SmemTall& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w & 1, wj = w >> 1, half = lane >> 5;
+  const OpRef at{p.a.p + ta * p.a_tile, p.a.ld, 0, p.a.cols - ta * TALL};
+  AccTall acc;
+  gemm_tile_tall<true>(at, bo, p.K, sm, acc);
+  const bool vec4 = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
+  auto put = [&](const floatx16& t, int ii, int jj) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float v[4] = {t[4 * r4], t[4 * r4 + 1], t[4 * r4 + 2], t[4 * r4 + 3]};
+      quad_transpose(v, lane);
+      const int row = ta * TALL + wi * 192 + ii * 32 + 8 * r4 + 4 * half + (lane & 3);
+      const int col0 = tb * TILE + wj * 128 + jj * 32 + (lane & 28);
+      if (row >= p.c_rows) continue;
+      float* const c = p.C + (size_t)row * p.ldc + col0;
+      if (vec4 && col0 + 4 <= p.c_cols) {
+        *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col0 + e < p.c_cols) c[e] = v[e];
+      }
+    }
+  };
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) put(acc.v[ii][jj], 4 + ii, jj);
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) put(acc.a[ii][jj], ii, jj);
+}
+
 template <bool SKIP, bool VEC>
 __device__ __forceinline__ void grads_task(const GemmProb& p0, const GemmProb& p1, int b,
-                                           Smem& sm) {
+                                           SmemTall& smt) {
+  Smem& sm = *reinterpret_cast<Smem*>(&smt);
   const bool second = b >= p0.nl;
   const GemmProb p = second ? p1 : p0;
   if (second) b -= p0.nl;
@@ -428,6 +471,10 @@ __device__ __forceinline__ void grads_task(const GemmProb& p0, const GemmProb& p
   const OpRef a{p.a.p + ta * p.a_tile + (size_t)kb0 * 8 * 8192, p.a.ld, p.a.rows, p.a.cols};
   const OpRef bo{p.b.p + tb * p.b_tile + (size_t)kb0 * TILE * p.b.ld, p.b.ld,
                  p.b.rows - kb0 * TILE, p.b.cols - tb * TILE};
+  if (VEC && !SKIP && second && p.tall) {
+    dw_tall_task(p, ta, tb, bo, smt);
+    return;
+  }
   const int* kf = SKIP ? p.kflags + (size_t)ta * p.fa + (size_t)kb0 * p.fk : nullptr;
   floatx16 acc[4][4];
   if (!second)
@@ -493,7 +540,7 @@ __device__ __forceinline__ void grads_task(const GemmProb& p0, const GemmProb& p
 
 template <bool SKIP, bool VEC>
 __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
-  __shared__ Smem sm;
+  __shared__ SmemTall sm;  // the 256-row tasks use its first 128 KB
   grads_task<SKIP, VEC>(p0, p1, blockIdx.x, sm);
 }
 
@@ -507,7 +554,7 @@ template <bool FILTER, bool CAP>
 __global__ __launch_bounds__(NT, 1) void k_bwd_fused(GemmProb p0, GemmProb p1, RecArgs r) {
   __shared__ SmemTall sm;
   const int b = blockIdx.x, ng = p0.nl + p1.nl;
-  if (b < ng) grads_task<false, true>(p0, p1, b, *reinterpret_cast<Smem*>(&sm));
+  if (b < ng) grads_task<false, true>(p0, p1, b, sm);
   else recompute_tall_tile<FILTER, CAP>(r, b - ng, sm);
 }
 
@@ -623,7 +670,7 @@ static int tall_chunk(int Vc, int nMt) {
 // The dh / dW problems of one vocab chunk [v0, v0 + vlen) over the gradient
 // buffer G (see the kernels above for the operand forms).
 static void grads_probs(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* G, GemmProb& dh,
-                        GemmProb& dw, DhSplit& sp) {
+                        GemmProb& dw, DhSplit& sp, bool tall_dw = false) {
   const int nDt = a.Dpad / kTile;
   const int nkbV = a.Vc / 32;
   const int nvt = (vlen + kTile - 1) / kTile;
@@ -635,10 +682,19 @@ static void grads_probs(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* 
       sp.ks == 1 ? pad8(nT) : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
   dh = GemmProb{OpRef{G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
                 (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, dh_nl, a.flags,
-                fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P};
+                fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P, 0};
   dw = GemmProb{OpRef{G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
                 (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
-                a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr};
+                a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr, 0};
+  if (tall_dw) {  // 384-row vocab tiles: 12 blocks of G each
+    const int nvt3 = (vlen + TALL - 1) / TALL;
+    dw.a.cols = nkbV * 32;
+    dw.a_tile = (size_t)12 * 8192;
+    dw.nA = nvt3;
+    dw.nl = pad8(nvt3 * nDt);
+    dw.n_full = nvt3 * nDt;
+    dw.tall = 1;
+  }
 }
 
 static RecArgs rec_args(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* G) {
@@ -696,7 +752,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       const int v0 = chunks[c].first, vlen = chunks[c].second;
       GemmProb dh, dw;
       DhSplit sp;
-      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp);
+      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp, true);
       if (c + 1 < nch) {
         const int v1 = chunks[c + 1].first;
         const RecArgs r = rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]);

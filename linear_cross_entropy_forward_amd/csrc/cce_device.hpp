@@ -799,6 +799,105 @@ __device__ __forceinline__ void tall_mfma(const FragsTall& f, int q, AccTall& ac
   else mfma_vgpr(acc.v[i - 4][j], f.a[i], f.b[j]);
 }
 
+// Direct-to-LDS loads of one K-slice of a transposed blocked operand (OP_KBLK)
+// 384 columns wide (the dW contraction's A = G^T over a tall vocabulary tile):
+// 32 k-rows of 768 bytes (48 16-byte chunks).  Lane L of instruction p (0..5)
+// of wave w fills LDS chunk g = 64 (6 w + p) + L, i.e. k-row g / 48 at position
+// g % 48, with the global chunk (g % 48) ^ kswz(k-row) (the swizzle of the K
+// forms; it changes only the low 4 bits, so chunks stay inside the row).
+// Chunk c of k-row kr is 8 columns of block c / 4: byte (c / 4) 16384 + 64 kr +
+// 16 (c % 4) from the slice's base.  Blocks at or past nvb (the tile's valid
+// 32-column blocks) read as zero: the resource ends there.
+struct DmaKblkTall {
+  const u16* base;
+  int ld;   // blocks per 256-row tile of X
+  int nvb;  // valid blocks of this tile (1..12)
+  int voff[6];
+  unsigned ldsw;
+  struct Slice {
+    i32x4 rs;
+  };
+  __device__ __forceinline__ void init(const OpRef& op, int, int lane, int w) {
+    base = op.p;
+    ld = op.ld;
+    const int nb = (op.cols + 31) >> 5;
+    nvb = nb < 12 ? nb : 12;
+    ldsw = (unsigned)__builtin_amdgcn_readfirstlane(w * 6144);
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      const int g = 64 * (6 * w + p) + lane;
+      const int kr = g / 48;
+      const int c = (g % 48) ^ kswz(kr);
+      voff[p] = (c >> 2) * 16384 + kr * 64 + (c & 3) * 16;
+    }
+  }
+  __device__ __forceinline__ Slice slice(int k0) const {
+    Slice sl;
+    const u16* sb = base + (size_t)(k0 >> 8) * ld * 8192 + (size_t)(k0 & 255) * 32;
+    sl.rs = make_rsrc(sb, (unsigned)nvb * 16384u);
+    return sl;
+  }
+  __device__ __forceinline__ void issue(const Slice& sl, unsigned dst, int p) const {
+    dma16(sl.rs, voff[p], dst + ldsw + p * 1024, 0);
+  }
+  __device__ __forceinline__ void issue_all(int k0, unsigned dst) const {
+    const Slice sl = slice(k0);
+#pragma unroll
+    for (int p = 0; p < 6; ++p) issue(sl, dst, p);
+  }
+};
+
+// Fragment offsets of the K forms in a tall stage: A (768-byte k-rows, the
+// 384 columns of DmaKblkTall) per MFMA tile t, and B (512-byte k-rows, a K-form
+// operand of 256 columns after the A region; tile j at b ^ (j << 6)).  The
+// transposing read as in FragAddr: in each 16-lane group, lane s points at
+// k-row kr0 + s/4 and column i0 + 4 (s % 4); two reads 4 k-rows apart give the
+// lane's 8 K elements; lanes 16..31 take i0 + 16, lanes 32..63 K elements
+// 8..15 (k-rows + 8).  Sub-step 1 is 16 k-rows further.
+struct FragAddrKTall {
+  int a[6];
+  int b;
+  __device__ __forceinline__ void init(int lane, int wi, int wj) {
+    const int s = lane & 15, gi = (lane >> 4) & 1, half = lane >> 5;
+    const int kr = 8 * half + (s >> 2);
+    const int c0 = 2 * gi + ((s >> 1) & 1);
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+      a[t] = kr * 768 + (((24 * wi + 4 * t + c0) ^ kswz(kr)) << 4) + 8 * (s & 1);
+    b = TALL_A_BYTES + kr * 512 + ((c0 ^ kswz(kr)) << 4) + 8 * (s & 1) + wj * 256;
+  }
+};
+
+__device__ __forceinline__ bf16x8 read_tr_frag_w(const unsigned char* p, int second) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + second));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Fragment r (0..9) of a K-form tall sub-step, in the consuming order A0, B0..B3, A1..A5.
+__device__ __forceinline__ void tall_read_frag(const unsigned char* stage, const FragAddrKTall& fa,
+                                               int sub, int r, FragsTall& f) {
+  if (r == 0) f.a[0] = read_tr_frag_w(stage + fa.a[0] + sub * 12288, 3072);
+  else if (r < 5) f.b[r - 1] = read_tr_frag(stage + ((fa.b ^ ((r - 1) << 6)) + sub * 8192));
+  else f.a[r - 4] = read_tr_frag_w(stage + fa.a[r - 4] + sub * 12288, 3072);
+}
+
+// Operand forms of a tall tile: row-major A and B (the forward and the
+// recompute), or A = the transpose of a blocked matrix and B K-major (dW).
+template <bool KF>
+struct TallForms {
+  typedef DmaOperand<OP_ROW, false, 96> DA;
+  typedef DmaOperand<OP_ROW, false, 64> DB;
+  typedef FragAddrTall FA;
+};
+template <>
+struct TallForms<true> {
+  typedef DmaKblkTall DA;
+  typedef DmaOperand<OP_KROW, false, 64> DB;
+  typedef FragAddrKTall FA;
+};
+
 // One K step (slice kt in `cur`, kt+1 in `nxt`, kt+3 loaded into `far`):
 //   sub-step 0: 24 MFMAs; after even q < 20 one fragment read of sub-step 1,
 //     after q = 3, 7, .., 23 one of the 6 A loads of slice kt+3
@@ -806,12 +905,14 @@ __device__ __forceinline__ void tall_mfma(const FragsTall& f, int q, AccTall& ac
 //   and the 6 just issued), barrier
 //   sub-step 1: 24 MFMAs; after even q < 20 one read of slice kt+1's first
 //     fragments, after q = 5, 11, 17, 23 one of the 4 B loads of slice kt+3.
-__device__ __forceinline__ void tall_step(const DmaOperand<OP_ROW, false, 96>& da,
-                                          const DmaOperand<OP_ROW, false, 64>& db,
-                                          const FragAddrTall& fa, int kn, const unsigned char* cur,
-                                          const unsigned char* nxt, unsigned far, FragsTall& f0,
-                                          FragsTall& f1, AccTall& acc) {
-  const DmaOperand<OP_ROW, false, 96>::Slice sa = da.slice(kn);
+template <bool KF>
+__device__ __forceinline__ void tall_step(const typename TallForms<KF>::DA& da,
+                                          const typename TallForms<KF>::DB& db,
+                                          const typename TallForms<KF>::FA& fa, int kn,
+                                          const unsigned char* cur, const unsigned char* nxt,
+                                          unsigned far, FragsTall& f0, FragsTall& f1,
+                                          AccTall& acc) {
+  const typename TallForms<KF>::DA::Slice sa = da.slice(kn);
 #pragma unroll
   for (int q = 0; q < 24; ++q) {
     tall_mfma(f0, q, acc);
@@ -821,7 +922,7 @@ __device__ __forceinline__ void tall_step(const DmaOperand<OP_ROW, false, 96>& d
   }
   CCE_WAIT_VMCNT(16);  // slice kt+1 landed (slice kt+2 and the A half of kt+3 may be in flight)
   ring_barrier();
-  const DmaOperand<OP_ROW, false, 64>::Slice sb = db.slice(kn);
+  const typename TallForms<KF>::DB::Slice sb = db.slice(kn);
 #pragma unroll
   for (int q = 0; q < 24; ++q) {
     tall_mfma(f1, q, acc);
@@ -831,22 +932,26 @@ __device__ __forceinline__ void tall_step(const DmaOperand<OP_ROW, false, 96>& d
   }
 }
 
-// acc = A[0:384, 0:K] . B[0:256, 0:K]^T, K % 32 == 0, both operands 16-byte
-// aligned row-major (rows past A.rows / B.rows read as zero).  Ends with every
-// load drained, a barrier (LDS free) and the VGPR accumulators readable.
+// acc = A[0:384, 0:K] . B[0:256, 0:K]^T, K % 32 == 0.  !KF: both operands
+// 16-byte aligned row-major (rows past A.rows / B.rows read as zero).  KF: A is
+// the transpose of a blocked matrix (OP_KBLK; A.cols = valid columns of the
+// tile) and B is K-major (OP_KROW), with K a multiple of 256 (whole blocks).
+// Ends with every load drained, a barrier (LDS free) and the VGPR accumulators
+// readable.
+template <bool KF>
 __device__ __forceinline__ void gemm_tile_tall(const OpRef& A, const OpRef& B, int K, SmemTall& sm,
                                                AccTall& acc) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   tall_zero(acc);
-  FragAddrTall fa;
+  typename TallForms<KF>::FA fa;
   fa.init(lane, w & 1, w >> 1);
   unsigned char* ring = sm.raw;
   unsigned ring_lds = lds_addr(ring);
   const int nk = K / BK;
-  DmaOperand<OP_ROW, false, 96> da;
-  DmaOperand<OP_ROW, false, 64> db;
+  typename TallForms<KF>::DA da;
+  typename TallForms<KF>::DB db;
   da.init(A, K, lane, w);
   db.init(B, K, lane, w);
   asm volatile("" : "+s"(ring_lds));
@@ -868,9 +973,9 @@ __device__ __forceinline__ void gemm_tile_tall(const OpRef& A, const OpRef& B, i
     for (int j = 0; j < NSTAGE; ++j) {
       const int kt = kt0 + j;
       if (kt < nk)
-        tall_step(da, db, fa, min((kt + 3) * BK, klast), ring + j * TALL_STAGE,
-                  ring + ((j + 1) & 3) * TALL_STAGE, ring_lds + ((j + 3) & 3) * TALL_STAGE, f0, f1,
-                  acc);
+        tall_step<KF>(da, db, fa, min((kt + 3) * BK, klast), ring + j * TALL_STAGE,
+                      ring + ((j + 1) & 3) * TALL_STAGE, ring_lds + ((j + 3) & 3) * TALL_STAGE, f0,
+                      f1, acc);
     }
   }
   CCE_WAIT_VMCNT(0);

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NT, 1) void k_fwd_tall(const u16* __restrict__ H,
     const int hrows = min(TILE, M - mt_ * TILE);
     const int v0 = t * TALL;
     AccTall acc;
-    gemm_tile_tall(OpRef{W + (size_t)v0 * D_, D_, min(TALL, V - v0), D_},
+    gemm_tile_tall<false>(OpRef{W + (size_t)v0 * D_, D_, min(TALL, V - v0), D_},
                    OpRef{Hb, D_, hrows, D_}, D_, sm, acc);
     const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;  // the cap is taken in the update
     // the ring is drained (gemm_tile_tall ended with a barrier); each wave

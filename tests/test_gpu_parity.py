@@ -121,6 +121,12 @@ RAGGED = [
     ([(100, 250, 240, 10)], 128, 33000, "zipf", 1.0, WL.SCOPE_FULL),     # 3 M tiles, 3 chunks
     ([(0, 1, 1)], 8, 1, "uniform", 1.0, WL.SCOPE_FULL),                  # V = 1, M = 2
     ([(3, 2, 2, 1)] * 40, 64, 300, "uniform", 1.0, WL.SCOPE_RESPONSE),   # many pairs
+    # pipelined backward (two gradient buffers), 384-row vocab tiles ragged in every chunk:
+    # chunks 16384 + 15353, one partial D tile
+    ([(13, 40, 37, 5), (0, 21, 19)], 96, 31737, "zipf", 1.0, WL.SCOPE_FULL),
+    # 32 token tiles: 15360-wide chunk step (whole rounds of tall recompute tiles), the last
+    # chunk takes the 16377-entry remainder
+    ([(2047, 3072, 3072, 1)], 32, 31737, "zipf", 1.0, WL.SCOPE_FULL),
 ]
 
 
