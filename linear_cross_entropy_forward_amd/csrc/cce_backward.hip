@@ -752,7 +752,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       const int v0 = chunks[c].first, vlen = chunks[c].second;
       GemmProb dh, dw;
       DhSplit sp;
-      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp, true);
+      // 384-row dW tiles inside the pipelined launches; the last chunk's
+      // contractions run alone, where 256-row dW tiles pack into whole rounds
+      // (at 16384 wide: 320 dh tasks of two units and 640 dW tasks of one)
+      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp, c + 1 < nch);
       if (c + 1 < nch) {
         const int v1 = chunks[c + 1].first;
         const RecArgs r = rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]);
