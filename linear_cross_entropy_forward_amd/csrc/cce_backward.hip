@@ -716,11 +716,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   const int nkbV = a.Vc / 32;
   const bool filt = a.filter_eps > 0.f;
   const bool cap = a.softcap > 0.f;
-#ifdef CCE_NO_TALL
-  const bool tall = false;
-#else
+  // tall recompute tiles (and the pipelined backward) need aligned row-major
+  // operands with D % 32 == 0, and no tile skip (kept per 256x256 tile)
   const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
-#endif
   const int vstep = tall ? tall_chunk(a.Vc, a.nMt) : a.Vc;
   // the vocabulary chunks; the last one takes whatever is left when it fits
   // the workspace width (no short remainder chunk that runs the chip a

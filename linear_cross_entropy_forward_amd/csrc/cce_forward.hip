@@ -9,12 +9,13 @@
 // is cap * tanh(z / cap) before any of this.
 //
 // Work split: workgroup (mt, split) owns 256 token rows and a contiguous run of
-// T full vocab tiles of 256.  Each lane keeps (m, s) for the 4 tokens it owns
-// across all of its tiles; at the end the two lanes and two waves that share a
-// token merge, and the split writes one (m, s) pair per token into
-// partials[split][Mpad].  A ragged last vocab tile (V % 256 != 0) is handled
-// by a separate launch of the same kernel that masks the rows past V and
-// writes one more partial slot, so the main kernel carries no masking.  The
+// T vocab tiles (384 rows each in the tall kernel, 256 in k_fwd).  Each lane
+// keeps (m, s) for the 4 tokens it owns across all of its tiles; at the end the
+// two lanes and two waves that share a token merge, and the split writes one
+// (m, s) pair per token into partials[split][Mpad].  The tall kernel masks the
+// rows past V in its last tile (outside the K loop); k_fwd runs full tiles only
+// and takes a ragged last tile (V % 256 != 0) in a second launch of the same
+// kernel that masks the rows past V and writes one more partial slot.  The
 // target logit is one dot product per row, computed by its own small kernel.
 // The merge kernel combines the partials of a row in a fixed order: results
 // are deterministic and nothing depends on atomics.
@@ -439,11 +440,7 @@ void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {
 }
 
 bool fwd_use_tall(const FwdArgs& a) {
-#ifdef CCE_NO_TALL
-  return false;
-#else
   return a.vec && a.D % BK == 0 && a.bm == nullptr;
-#endif
 }
 
 hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {
