@@ -6,16 +6,20 @@
 // — design", lever 1 spec (backward).  With coef = -dL/dlogp:
 //   G[i, v] = coef_i (softmax(i, v) - [v = y_i]),  dh = G W,  dW = G^T h.
 //
-// The vocabulary is walked in chunks of kVocabChunk entries.  Per chunk:
+// The vocabulary is walked in chunks of at most kVocabChunk entries.  Per
+// chunk:
 //   1. recompute z = h W[chunk]^T, G = coef (softmax - onehot) (times
 //      sech^2(z / c) under a softcap c), optional filter / tile skip; G
 //      written as bf16 (RNE)                                         MFMA
 //   2. dh (+)= G W[chunk] and dW[chunk] = G^T h, one launch          MFMA
-// All three contractions run on the same GEMM core; the transposed operands
-// of step 2 (W[chunk] and h with K = vocab / tokens, and G^T) are read in
-// place with transposing LDS reads, so nothing but G is materialised.  dh
-// accumulates across chunks in stream order, so no atomics are used and
-// results are deterministic.  The workspace (G) depends on M but not on V.
+// All three contractions run on the same GEMM cores (256 x 256 tiles, or the
+// 384 x 256 tall tiles where the operands allow); the transposed operands of
+// step 2 (W[chunk] and h with K = vocab / tokens, and G^T) are read in place
+// with transposing LDS reads, so nothing but G is materialised.  With tall
+// tiles the two steps are pipelined over two G buffers: one launch runs chunk
+// c's step 2 and chunk c+1's step 1.  dh accumulates across chunks in stream
+// order, so no atomics are used and results are deterministic.  The workspace
+// (G, or two of them) depends on M but not on V.
 //
 // G is stored BLOCKED: with Vc chunk columns, element (t, v) sits at
 // ((t / 256) * (Vc / 32) + v / 32) * 8192 + (t % 256) * 32 + v % 32, so every

@@ -693,8 +693,9 @@ __device__ __forceinline__ void gemm_tile(const OpRef& A, const OpRef& B, int K,
 }
 
 // ---------------------------------------------------------------------------
-// Tall tile: A 384 rows x B 256 rows, both row-major [i][k] with K % 32 == 0
-// (the forward and the recompute: A = vocabulary rows, B = token rows).
+// Tall tile: A 384 rows x B 256 rows, K % 32 == 0 (TallForms below: both
+// row-major for the forward and the recompute, A = vocabulary rows and B =
+// token rows; A the transposed gradient buffer and B K-major for dW).
 //
 // The core loop above is bound by the operand stream through each CU (bytes
 // per MFMA), not by the MFMAs.  A 384 x 256 tile needs 40 KB per 32-wide
@@ -709,13 +710,15 @@ __device__ __forceinline__ void gemm_tile(const OpRef& A, const OpRef& B, int K,
 // statement that names them as operands after they are zeroed (VALU write ->
 // MFMA read of SrcC) and after the K loop (MFMA write -> VALU read; 8-pass
 // MFMA: 11 wait states, 24 given).  Within the loop an accumulator is only
-// touched by its own MFMA, 24 MFMAs apart, and the A / B fragments are written
-// by LDS reads only, which the compiler's waitcnt insertion orders before the
-// MFMAs that read them.
+// touched by its own MFMA, 24 MFMAs apart, and the A / B fragments come from
+// LDS reads, which the compiler's waitcnt insertion orders before the MFMAs
+// that read them (a VALU write of a fragment register would need 2 wait states
+// before such an MFMA; the generated code is checked to have none).
 //
 // LDS: 4 stages of 40 KB (A 24 KB then B 16 KB), the whole 160 KB; the
 // layouts, the swizzle and the order of the K step are those of the core loop,
-// with 6 A fragment reads and 6 A loads per sub-step.
+// with 24 MFMAs and 10 fragment reads per sub-step, the 6 A loads of a slice in
+// sub-step 0 and its 4 B loads in sub-step 1.
 // ---------------------------------------------------------------------------
 constexpr int TALL = 384;
 constexpr int TALL_A_BYTES = TALL * BK * 2;            // 24 KB
