@@ -100,8 +100,12 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
     const int hrows = min(TILE, M - mt_ * TILE);
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_},
-                                 OpRef{Hb, D_, hrows, D_}, D_, nullptr, 0, sm, acc);
+    if (VEC && !KTAIL && (D_ % 64) == 0)  // 64-wide K-slices: 128 bytes a row per load
+      gemm_tile64(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_}, OpRef{Hb, D_, hrows, D_},
+                  D_, sm.raw, acc);
+    else
+      gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_},
+                                   OpRef{Hb, D_, hrows, D_}, D_, nullptr, 0, sm, acc);
     if (CAP) {
       const float k2 = 2.f * LOG2E / softcap;
 #pragma unroll
@@ -439,8 +443,14 @@ void fwd_split_tiles(int nMt, int nVt, int& S, int& T) {
   S = (nVt + T - 1) / T;
 }
 
+// The 256 x 256 tiles with 64-wide K-slices (k_fwd, D % 64 == 0) stream their
+// operands faster than the tall tiles with 32-wide slices, but pay a longer
+// prologue per tile: they are taken when each workgroup runs at least 32 vocab
+// tiles (the Gemma-4B head: 128), the tall tiles otherwise.
 bool fwd_use_tall(const FwdArgs& a) {
-  return a.vec && a.D % BK == 0 && a.bm == nullptr;
+  if (!(a.vec && a.D % BK == 0 && a.bm == nullptr)) return false;
+  if (a.D % 64 == 0 && a.T >= 32) return false;
+  return true;
 }
 
 hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {

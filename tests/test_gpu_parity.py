@@ -142,6 +142,29 @@ def test_ragged_and_edge_shapes(device, case):
     check_full(wl, g, o, scope, tag=f"ragged{case}")
 
 
+def test_forward_many_tiles_per_workgroup(device):
+    """The forward at a shape where every workgroup runs 32 vocab tiles (8192
+    rows, 65613 vocab entries with a ragged tail tile, D = 64): the 256x256 tiles
+    with 64-wide K-slices, against the oracle's forward on every row, and with the
+    softcap; the same head at D = 96 (D % 64 != 0) takes the tall tiles."""
+    for D, cap in ((64, 0.0), (64, 25.0), (96, 0.0)):
+        wl = WL.make_custom([(2047, 3072, 3072, 1)], D=D, V=65613, seed=470 + D, hidden_scale=2.0,
+                            w_std=0.05, targets="zipf")
+        say(f"[gpu] forward, many tiles per workgroup: M={wl.M} V={wl.V} D={D} softcap={cap}")
+        head = B.Head(wl.M, wl.V, wl.D, device)
+        h, W, y, seg = upload(wl, device)
+        head.clear_status()
+        logp, lse = head.forward(h, W, y, softcap=cap)
+        torch.cuda.synchronize()
+        assert head.read_status() == 0
+        ref_logp, ref_lse = O.forward(wl.h64(), wl.W64(), wl.y, softcap=cap)
+        valid = wl.y >= 0
+        check_rows(lse.cpu().numpy(), ref_lse, f"D={D} cap={cap} lse")
+        check_rows(logp.cpu().numpy()[valid], ref_logp[valid], f"D={D} cap={cap} logp")
+        del head, h, W, y, seg
+        torch.cuda.empty_cache()
+
+
 def test_small_config_full(device):
     wl = WL.make_workload("small_1b")
     say(f"[gpu] small_1b M={wl.M} V={wl.V} D={wl.D}")
