@@ -290,10 +290,18 @@ def main():
     fwd_flops = 2.0 * wl.M * wl.V * wl.D
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tflops = (n_contr - 1) * fwd_flops / (bwd_ms * 1e-3) / 1e12
-    # the forward runs 384 x 256 tiles (k_fwd_tall) when D % 32 == 0 and no block
-    # maximum is saved, else 256 x 256 tiles (k_fwd); the recompute likewise
-    # (k_recompute_tall) when no tile is skipped
-    fwd_kernel = "k_fwd_tall" if (wl.D % 32 == 0 and not args.block_max) else "k_fwd"
+    # the forward runs 256 x 256 tiles with 64-wide K-slices (k_fwd) when D % 64 == 0
+    # and each workgroup runs >= 32 vocab tiles, else 384 x 256 tiles (k_fwd_tall)
+    # when D % 32 == 0 and no block maximum is saved, else k_fwd; the recompute
+    # runs k_recompute_tall when D % 32 == 0 and no tile is skipped
+    n_mt = (wl.M + 255) // 256
+    full = wl.V // 256
+    smax = max(1, min(256 // n_mt, full)) if full > 0 else 1
+    tiles_per_wg = (full + smax - 1) // smax if full > 0 else 0
+    if wl.D % 64 == 0 and tiles_per_wg >= 32:
+        fwd_kernel = "k_fwd"
+    else:
+        fwd_kernel = "k_fwd_tall" if (wl.D % 32 == 0 and not args.block_max) else "k_fwd"
     rec_kernel = "k_recompute_tall" if (wl.D % 32 == 0 and not feps > 0) else "k_recompute"
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
