@@ -45,9 +45,10 @@ reason in the design notes of the repository):
     forward and backward are the bf16 head's on round_bf16(dequantize(...)).
 
 Every function here has a pin in the test-suite (closed forms, library special
-cases, finite differences, brute force, invariants); none is "parity unpinned"
-except the filtered-gradient mode, whose deviation from the exact gradient is
-reported, not gated.
+cases, finite differences, brute force, invariants); none is "parity unpinned".
+The filtered-gradient mode is pinned by brute force on a tiny case (scalar
+loops, an entry exactly at eps, a target far below it); how far it moves the
+gradient from the exact one is reported, not gated.
 """
 from __future__ import annotations
 

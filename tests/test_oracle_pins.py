@@ -467,6 +467,40 @@ def test_filter_mode_drops_only_small_entries():
     assert changed.sum() > 0
 
 
+def test_filter_mode_brute_force():
+    """The filtered gradient on a tiny case, written out with scalar loops: a
+    non-target entry whose softmax value is below eps contributes nothing, every
+    other entry is coef * (p - onehot).  Drops exactly that set (an entry at
+    p >= eps stays), and the target is kept however small its p."""
+    rng = np.random.default_rng(21)
+    M, V, D, eps = 5, 40, 6, 2e-2
+    H = rng.normal(size=(M, D)) * 1.5
+    W = rng.normal(size=(V, D))
+    y = np.array([3, 17, -1, 39, 0])
+    coef = np.array([0.7, -1.3, 0.4, 2.0, -0.2])
+    Z = H @ W.T
+    # make row 0's target tiny (it must survive the filter) and put one entry
+    # of row 1 exactly at the threshold (it must survive too: only p < eps drops)
+    Z[0, 3] = Z[0].max() - 30.0
+    zmax1 = Z[1].max()
+    ssum = sum(math.exp(Z[1, v] - zmax1) for v in range(V) if v != 5)
+    Z[1, 5] = zmax1 + math.log(eps * ssum / (1.0 - eps))
+    lse = np.array([max(Z[i]) + math.log(sum(math.exp(Z[i, v] - max(Z[i])) for v in range(V)))
+                    for i in range(M)])
+    G = O.grad_logits(Z, lse, y, coef, eps)
+    dropped = 0
+    for i in range(M):
+        for v in range(V):
+            p = math.exp(Z[i, v] - lse[i])
+            tgt = 1.0 if v == y[i] else 0.0
+            want = 0.0 if (p < eps and tgt == 0.0) else coef[i] * (p - tgt)
+            dropped += p < eps and tgt == 0.0
+            assert abs(G[i, v] - want) <= 1e-12 * max(1.0, abs(want)), (i, v)
+    assert math.exp(Z[1, 5] - lse[1]) == eps  # exactly at the threshold in this seeded case
+    assert G[1, 5] != 0.0 and G[0, 3] != 0.0
+    assert 0 < dropped < M * V
+
+
 # ----------------------------------------------------------------------------
 # input generators
 # ----------------------------------------------------------------------------
