@@ -303,6 +303,11 @@ def main():
     else:
         fwd_kernel = "k_fwd_tall" if (wl.D % 32 == 0 and not args.block_max) else "k_fwd"
     rec_kernel = "k_recompute_tall" if (wl.D % 32 == 0 and not feps > 0) else "k_recompute"
+    # the bf16 head with tall recompute tiles runs the pipelined backward: chunk 0's
+    # recompute alone, one fused launch per later chunk (dh / dW of chunk c and the
+    # recompute of c + 1), the last chunk's dh / dW alone
+    bwd_kernels = ("k_recompute_tall + k_bwd_fused + k_grads (cce_backward)"
+                   if rec_kernel == "k_recompute_tall" else f"{rec_kernel} + k_grads (cce_backward)")
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
         try:
@@ -353,7 +358,7 @@ def main():
         # the backward's kernels (per vocab chunk: recompute, then dh + dW) timed
         # together live around cce_backward: 3 contractions of 2*M*V*D FLOPs
         "roofline_backward": {"kernels": f"k_dequant + {rec_kernel} + k_grads (dh) (cce_backward_q)"
-                              if quant else f"{rec_kernel} + k_grads (cce_backward)",
+                              if quant else bwd_kernels,
                               "bound": "mfma", "achieved": round(bwd_tflops, 2),
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
