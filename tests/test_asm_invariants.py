@@ -1,5 +1,6 @@
-"""Invariants of the generated gfx950 code of the 384-row (tall) tiles (CPU only:
-hipcc cross-compiles the kernels to assembly, nothing runs).
+"""Invariants of the generated gfx950 code of the 384-row (tall) tiles and of the
+forward's 64-wide K-slice loop (CPU only: hipcc cross-compiles the kernels to
+assembly, nothing runs).
 
 The tall kernels keep a third of their MFMA accumulators in VGPRs and issue
 those MFMAs as inline assembly, which the compiler does not look inside.  The
@@ -223,3 +224,19 @@ def test_no_scratch_in_mfma_blocks(assembly):
             for b in blocks:
                 if any(t.startswith("v_mfma") for t in b):
                     assert not any("scratch_" in t for t in b), name
+
+
+def test_no_scratch_in_the_forward_64_wide_k_loop(assembly):
+    """The forward's 64-wide K-slice loop (256x256 tiles; in every k_fwd built
+    for aligned operands without a K tail, the only block with 128 MFMAs) holds
+    no scratch access either."""
+    asm = assembly["cce_forward.hip"]
+    seen = 0
+    for m in re.finditer(r"^(_Z\w*k_fwdILb1ELb0E\w*):", asm, re.M):
+        end = asm.find(".Lfunc_end", m.end())
+        for b in re.split(r"\n(?=\.LBB\w+:)", asm[m.end():end]):
+            lines = [t.split(";")[0].strip() for t in b.split("\n")]
+            if sum(t.startswith("v_mfma") for t in lines) >= 128:
+                seen += 1
+                assert not any("scratch_" in t for t in lines), m.group(1)
+    assert seen >= 8
