@@ -243,12 +243,27 @@ def orpo_pair_grad(lw: float, lr: float, lam: float):
 # "File-by-file changes" (nll = mean(-lw), or = mean(softplus(-logOdds)),
 # loss = nll + lambda*or; metrics loss/nll/or/accuracy/margin).
 # ----------------------------------------------------------------------------
-def epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope: int) -> Dict:
-    logp = np.asarray(logp, np.float64)
+def pair_row_sets(seg: np.ndarray, n_pairs: int):
+    """For each pair b: the ascending row indices of its CHOSEN, REJECTED and
+    PROMPT rows (the sets {i: pair_i = b, kind_i = K}).  Rows are grouped once
+    with a stable sort, so each pair costs only its own rows."""
     seg = np.asarray(seg, np.int64)
     kind = seg & 3
     pair = seg >> 2
+    order = np.argsort(pair, kind="stable")
+    bounds = np.searchsorted(pair[order], np.arange(int(n_pairs) + 1))
+    out = []
+    for b in range(int(n_pairs)):
+        idx = order[bounds[b]:bounds[b + 1]]
+        out.append(tuple(idx[kind[idx] == k] for k in (KIND_CHOSEN, KIND_REJECTED, KIND_PROMPT)))
+    return out
+
+
+def epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope: int) -> Dict:
+    logp = np.asarray(logp, np.float64)
+    seg = np.asarray(seg, np.int64)
     B = int(n_pairs)
+    sets = pair_row_sets(seg, B)
     Mw = np.zeros(B, np.int64)
     Mr = np.zeros(B, np.int64)
     Pm1 = np.zeros(B, np.int64)
@@ -262,10 +277,8 @@ def epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope:
     dlo_w = np.zeros(B)
     dlo_r = np.zeros(B)
     for b in range(B):
-        C = (pair == b) & (kind == KIND_CHOSEN)
-        R = (pair == b) & (kind == KIND_REJECTED)
-        Q = (pair == b) & (kind == KIND_PROMPT)
-        Mw[b], Mr[b], Pm1[b] = int(C.sum()), int(R.sum()), int(Q.sum())
+        C, R, Q = sets[b]
+        Mw[b], Mr[b], Pm1[b] = len(C), len(R), len(Q)
         if Mw[b] == 0 or Mr[b] == 0:
             raise ValueError(f"pair {b} has an empty response span")
         lw[b] = logp[C].sum() / Mw[b]
@@ -286,9 +299,7 @@ def epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, lam: float, scope:
     # coef_i = -dloss/dlogp_i
     coef = np.zeros(logp.shape[0])
     for b in range(B):
-        C = (pair == b) & (kind == KIND_CHOSEN)
-        R = (pair == b) & (kind == KIND_REJECTED)
-        Q = (pair == b) & (kind == KIND_PROMPT)
+        C, R, Q = sets[b]
         w_or = lam * (1.0 - sig[b])          # = -dloss_b/dlo (before 1/B)
         if scope == SCOPE_FULL:
             w_nll = 1.0 / (Pm1[b] + Mw[b])
@@ -351,19 +362,16 @@ def pref_epilogue(logp: np.ndarray, seg: np.ndarray, n_pairs: int, objective: in
                   nll_weight: float, lam: float, beta: float, gamma: float, scope: int) -> Dict:
     logp = np.asarray(logp, np.float64)
     seg = np.asarray(seg, np.int64)
-    kind = seg & 3
-    pair = seg >> 2
     B = int(n_pairs)
+    sets = pair_row_sets(seg, B)
     out = {k: np.zeros(B) for k in ("lw", "lr", "pm", "s", "pref_b", "nll_b")}
     Mw = np.zeros(B, np.int64)
     Mr = np.zeros(B, np.int64)
     Pm1 = np.zeros(B, np.int64)
     coef = np.zeros(logp.shape[0])
     for b in range(B):
-        C = (pair == b) & (kind == KIND_CHOSEN)
-        R = (pair == b) & (kind == KIND_REJECTED)
-        Q = (pair == b) & (kind == KIND_PROMPT)
-        Mw[b], Mr[b], Pm1[b] = int(C.sum()), int(R.sum()), int(Q.sum())
+        C, R, Q = sets[b]
+        Mw[b], Mr[b], Pm1[b] = len(C), len(R), len(Q)
         if Mw[b] == 0 or Mr[b] == 0:
             raise ValueError(f"pair {b} has an empty response span")
         lw = logp[C].sum() / Mw[b]

@@ -58,14 +58,45 @@ E = math.e
     # (-0.5, -0.5): log_odds = 0, L_OR = ln 2, sigma = 1/2.
     (-0.5, -0.5, 0.1, 0.0, math.log(2.0), 0.5 + 0.1 * math.log(2.0),
      -1.0 - 0.05 / (1 - math.exp(-0.5)), 0.05 / (1 - math.exp(-0.5))),
+    # (-1.5, -0.7), lambda 0.5: log_odds = -0.8 - ln((1 - e^-1.5) / (1 - e^-0.7)), worked by
+    # hand to 12 digits (and checked against 50-digit decimal arithmetic below)
+    (-1.5, -0.7, 0.5, -1.233858543883, 1.489404947951, 2.244702473976,
+     -1.498470371973, 0.769239755935),
 ])
 def test_p1_closed_form_scalars(lw, lr, lam, lo, lor, L, dlw, dlr):
-    assert O.log_odds(lw, lr) == pytest.approx(lo, rel=1e-13, abs=1e-14)
-    assert O.or_term(lw, lr) == pytest.approx(lor, rel=1e-13)
-    assert O.orpo_pair_loss(lw, lr, lam) == pytest.approx(L, rel=1e-13)
+    # the third point's values are printed to 12 digits: compare at that precision
+    rel = 1e-11 if lw == -1.5 else 1e-12
+    assert O.log_odds(lw, lr) == pytest.approx(lo, rel=max(rel, 1e-13), abs=1e-14)
+    assert O.or_term(lw, lr) == pytest.approx(lor, rel=max(rel, 1e-13))
+    assert O.orpo_pair_loss(lw, lr, lam) == pytest.approx(L, rel=max(rel, 1e-13))
     g = O.orpo_pair_grad(lw, lr, lam)
-    assert g[0] == pytest.approx(dlw, rel=1e-12)
-    assert g[1] == pytest.approx(dlr, rel=1e-12)
+    assert g[0] == pytest.approx(dlw, rel=rel)
+    assert g[1] == pytest.approx(dlr, rel=rel)
+
+
+def test_p1_third_point_in_decimal_arithmetic():
+    """(lw, lr) = (-1.5, -0.7), lambda 0.5, response scope, evaluated from the
+    definitions in 50-digit decimal arithmetic (no oracle code): log_odds,
+    L_OR = ln(1 + e^-log_odds), L = -lw + lambda L_OR, and the partials by the
+    chain rule, d log_odds/d l = 1 / (1 - e^l)."""
+    getcontext().prec = 50
+    lw, lr, lam = Decimal("-1.5"), Decimal("-0.7"), Decimal("0.5")
+    one = Decimal(1)
+    lo = (lw - lr) - ((one - lw.exp()).ln() - (one - lr.exp()).ln())
+    lor = (one + (-lo).exp()).ln()
+    L = -lw + lam * lor
+    sig = one / (one + (-lo).exp())
+    dlw = -one - lam * (one - sig) / (one - lw.exp())
+    dlr = lam * (one - sig) / (one - lr.exp())
+    assert float(lo) == pytest.approx(-1.233858543883, abs=5e-13)
+    assert float(lor) == pytest.approx(1.489404947951, abs=5e-13)
+    assert float(L) == pytest.approx(2.244702473976, abs=5e-13)
+    assert float(dlw) == pytest.approx(-1.498470371973, abs=5e-13)
+    assert float(dlr) == pytest.approx(0.769239755935, abs=5e-13)
+    g = O.orpo_pair_grad(-1.5, -0.7, 0.5)
+    assert O.orpo_pair_loss(-1.5, -0.7, 0.5) == pytest.approx(float(L), rel=1e-14)
+    assert g[0] == pytest.approx(float(dlw), rel=1e-13)
+    assert g[1] == pytest.approx(float(dlr), rel=1e-13)
 
 
 def test_oracle_regression_fixture():
@@ -890,3 +921,77 @@ def test_p14_block_skip_zeroes_exactly_the_dead_blocks():
     y2[3] = 9
     dead2 = O.dead_blocks(O.block_max(H, W, block=blk), lse, y2, 1e-4, block=blk)
     assert not dead2[0, 1] and dead2[1, 1]
+
+
+# ----------------------------------------------------------------------------
+# Row helpers (sampled checks at sizes where the whole oracle is too slow): each
+# equals the matching rows of the whole-matrix functions above, which the pins
+# above fix.  Subsets are unsorted, with a repeated index, so that an indexing
+# mistake (rows of one array taken against another's order) shows.
+# ----------------------------------------------------------------------------
+def _helper_case(seed):
+    rng = np.random.default_rng(seed)
+    M, V, D = 37, 53, 9
+    H = rng.standard_normal((M, D)) * 1.5
+    W = rng.standard_normal((V, D)) * 0.7
+    y = rng.integers(0, V, M)
+    y[[4, 11]] = -1
+    coef = rng.standard_normal(M)
+    coef[[4, 11]] = 0.0
+    rows = np.array([30, 2, 17, 4, 2, 36, 0, 11, 23])
+    vrows = np.array([52, 7, 0, 31, 7, 19, int(y[5]), int(y[6])])
+    return H, W, y, coef, rows, vrows
+
+
+@pytest.mark.parametrize("softcap,feps", [(0.0, 0.0), (0.0, 2e-2), (1.7, 0.0), (1.7, 2e-2)])
+def test_row_helpers_equal_the_whole_oracle(softcap, feps):
+    H, W, y, coef, rows, vrows = _helper_case(31)
+    logp, lse = O.forward(H, W, y, softcap)
+    lp_r, ls_r = O.forward_rows(H, W, y, rows, softcap)
+    np.testing.assert_allclose(lp_r, logp[rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(ls_r, lse[rows], rtol=1e-12)
+    dh, dW = O.backward(H, W, y, lse, coef, filter_eps=feps, softcap=softcap)
+    dh_r = O.backward_dh_rows(H, W, y, lse, coef, rows, filter_eps=feps, softcap=softcap)
+    np.testing.assert_allclose(dh_r, dh[rows], rtol=1e-12, atol=1e-15)
+    dW_r = O.backward_dW_rows(H, W, y, lse, coef, vrows, filter_eps=feps, softcap=softcap)
+    np.testing.assert_allclose(dW_r, dW[vrows], rtol=1e-12, atol=1e-15)
+    # the filter changes something in these cases (so the filtered branch is exercised)
+    if feps:
+        dh0, dW0 = O.backward(H, W, y, lse, coef, softcap=softcap)
+        assert not np.allclose(dh0[rows], dh_r) and not np.allclose(dW0[vrows], dW_r)
+
+
+# ----------------------------------------------------------------------------
+# P15: the softmax part of the gradient on its own.  With every target -1 the
+# gradient is G = coef * softmax (times sech^2 under a cap), which is the
+# gradient of sum_i coef_i lse_i: d lse_i / d z_iv = softmax_iv.  Pinned
+# against torch autograd (fp64, CPU) of that sum, written with logsumexp.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("softcap", [0.0, 2.5])
+def test_p15_softmax_part_is_the_gradient_of_weighted_lse(softcap):
+    import torch
+    rng = np.random.default_rng(41)
+    M, V, D = 13, 29, 7
+    H = rng.standard_normal((M, D)) * 1.3
+    W = rng.standard_normal((V, D)) * 0.8
+    coef = rng.standard_normal(M)
+    y = -np.ones(M, np.int64)
+    _, lse = O.forward(H, W, y, softcap)
+    dh, dW = O.backward(H, W, y, lse, coef, softcap=softcap)
+    Ht = torch.tensor(H, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    Z = Ht @ Wt.T
+    if softcap:
+        Z = softcap * torch.tanh(Z / softcap)
+    (torch.tensor(coef) * torch.logsumexp(Z, dim=1)).sum().backward()
+    np.testing.assert_allclose(dh, Ht.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+    # and the whole gradient with targets is this part minus the onehot part
+    y2 = rng.integers(0, V, M)
+    dh2, dW2 = O.backward(H, W, y2, lse, coef, softcap=softcap)
+    sech2 = O.dcapped(H @ W.T, softcap)[np.arange(M), y2]
+    onehot_dh = (coef * sech2)[:, None] * W[y2]
+    onehot_dW = np.zeros_like(W)
+    np.add.at(onehot_dW, y2, (coef * sech2)[:, None] * H)
+    np.testing.assert_allclose(dh2, dh - onehot_dh, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW2, dW - onehot_dW, rtol=1e-11, atol=1e-14)
