@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--block-max", action="store_true",
                     help="the forward saves the per-(vocab block, row) maximum and the backward "
                          "decides its block skip from it before recomputing a tile")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "k_fwd_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "kernel_traffic.json"))
+    ap.add_argument("--no-launch-timing", action="store_true",
+                    help="time the steps without the library's per-launch events")
     ap.add_argument("--v-sweep", action="store_true",
                     help="time one step and record workspace / peak device memory at "
                          "V in {32768, 65536, 131072, 262144} (M=8192, D=2560); one JSON line per V")
@@ -54,9 +56,14 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_KERNELS = ("k_fwd", "k_fwd_tall", "k_bwd_fused", "k_grads", "k_recompute_tall")
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, workload: str):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the forward kernel, scaled by
-    what the same counters read for the 1 GiB copy kernel of the same run."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the head's GEMM kernels,
+    averaged per kernel over its dispatches, each scaled by what the same counter
+    reads for the 1 GiB copy kernel of the same run (true bytes per counted
+    byte)."""
     import csv
     from linear_cross_entropy_forward_amd import binding as B
 
@@ -69,24 +76,52 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_json: str, workload: str):
             acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
         return acc
 
-    res = {}
+    def base_name(kname):
+        n = kname.split("(")[0].split("<")[0].strip()
+        return n.split("::")[-1].split(" ")[-1]
+
+    out = {"workload": workload, "kernel_source_hash": B.kernel_source_hash(), "kernels": {}}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         d = per_dispatch(path, counter)
-        fwd = [v for (i, n), v in d.items() if "k_fwd<" in n or "k_fwd_tall<" in n]
-        kname = "k_fwd_tall" if any("k_fwd_tall<" in n for (i, n) in d) else "k_fwd"
         copy = [v for (i, n), v in d.items() if "copyBuffer" in n or "copy" in n.lower()]
         copy = [v for v in copy if v > 1e5]          # the 1 GiB copy, not small transfers
-        if not fwd or not copy:
-            raise SystemExit(f"{path}: no forward or copy dispatch with {counter}")
-        scale = (1 << 30) / (max(copy) * 1024.0)      # true bytes per counted byte
-        res[counter] = {"kib_per_launch": sum(fwd) / len(fwd), "copy_kib": max(copy),
-                        "scale": scale, "bytes_per_launch": sum(fwd) / len(fwd) * 1024.0 * scale}
-    out = {"workload": workload, "kernel": kname, "kernel_source_hash": B.kernel_source_hash(),
-           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
-           "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]}
+        if not copy:
+            raise SystemExit(f"{path}: no copy dispatch with {counter}")
+        scale = (1 << 30) / (max(copy) * 1024.0)
+        for kn in TRAFFIC_KERNELS:
+            vals = [v for (i, n), v in d.items() if base_name(n) == kn]
+            if not vals:
+                continue
+            e = out["kernels"].setdefault(kn, {"dispatches": len(vals)})
+            e[counter] = {"kib_per_launch": sum(vals) / len(vals), "copy_kib": max(copy),
+                          "scale": scale, "bytes_per_launch": sum(vals) / len(vals) * 1024.0 * scale}
+    for e in out["kernels"].values():
+        if "FETCH_SIZE" in e and "WRITE_SIZE" in e:
+            e["bytes_per_launch"] = e["FETCH_SIZE"]["bytes_per_launch"] + e["WRITE_SIZE"]["bytes_per_launch"]
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def host_description():
+    """CPU model name and the BLAS numpy calls (for the CPU baseline)."""
+    import numpy as np
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    return model, blas
 
 
 def cpu_baseline(wl, rows: int):
@@ -118,7 +153,9 @@ def cpu_baseline(wl, rows: int):
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit():
         cores = min(cores, int(omp))
+    model, blas = host_description()
     return {"value": len(idx) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"{len(idx)} rows of {wl.name} (one pair, same span mix), full V={wl.V} and "
                       f"D={wl.D}; fp64 forward+epilogue+backward; {dt:.2f} s"}
 
@@ -179,6 +216,37 @@ def v_sweep(steps: int):
         print(json.dumps(rec), flush=True)
         del h, W, y, seg, dh, dW, logp, lse, coef, out5, pst, head
         torch.cuda.empty_cache()
+
+
+def filter_deviation(head, h, W, y, lse, coef, feps, dh, dW, bwd_ms, softcap, bmax, stream):
+    """How far the filtered gradient of the timed steps (in dh, dW) is from the
+    exact one, both from the library (relative L2 over every entry), and the
+    backward's effective speed-up (exact backward time over the filtered one,
+    medians of a few backward calls each, outside the timed region)."""
+    import numpy as np
+    import torch
+    dh_x, dW_x = head.backward(h, W, y, lse, coef, 0.0, 0.0, stream=stream, softcap=softcap)
+    torch.cuda.synchronize()
+
+    def rl2(a, b):
+        return float(torch.linalg.vector_norm((a - b).double()) / torch.linalg.vector_norm(b.double()))
+
+    dev = {"eps": feps, "dh_rel_l2_vs_exact": rl2(dh, dh_x), "dW_rel_l2_vs_exact": rl2(dW, dW_x),
+           "reference": "the library's own exact backward (filter and block skip off) on the same inputs"}
+    del dW_x
+    torch.cuda.empty_cache()
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        head.backward(h, W, y, lse, coef, 0.0, 0.0, dh_x, dW, stream=stream, softcap=softcap)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    dev["backward_ms_exact"] = round(float(np.median(times)), 4)
+    dev["backward_ms_filtered"] = round(bwd_ms, 4)
+    dev["speedup"] = round(dev["backward_ms_exact"] / bwd_ms, 4)
+    return dev
 
 
 def main():
@@ -261,6 +329,7 @@ def main():
     status = head.read_status()
     print(f"[bench] warmup done, status={status}", file=sys.stderr, flush=True)
 
+    # pass 1 (the headline): K steps, each bracketed by events on the stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -271,13 +340,24 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # pass 2: the same K steps with every library launch bracketed by its own events
+    # (recording them between launches adds a few microseconds a launch, so the
+    # headline comes from pass 1)
+    timer = None if args.no_launch_timing else B.LaunchTimer(capacity=96 * args.steps)
+    if timer is not None:
+        with timer:
+            for k in range(args.steps):
+                one_step()
+        torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    epi_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (fwd {fwd_ms:.3f}, epi {epi_ms:.3f}, "
-          f"bwd {bwd_ms:.3f}); wall {wall:.2f} s", file=sys.stderr, flush=True)
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms_step = float(np.median(step_ms))
+    fwd_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    epi_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    bwd_ms = float(np.median([e[2].elapsed_time(e[3]) for e in evs]))
+    print(f"[bench] {args.steps} steps: median {ms_step:.3f} ms/step, mean {ms_total / args.steps:.3f} "
+          f"(fwd {fwd_ms:.3f}, epi {epi_ms:.3f}, bwd {bwd_ms:.3f}); wall {wall:.2f} s",
+          file=sys.stderr, flush=True)
 
     # contractions per step: forward logits, recomputed logits, dh, and dW (bf16 head
     # only: the quantised head is frozen)
@@ -285,38 +365,54 @@ def main():
     flops = 2.0 * n_contr * wl.M * wl.V * wl.D
     tflops = flops / (ms_step * 1e-3) / 1e12
     tokens_s = wl.M / (ms_step * 1e-3)
-    # the longest single launch, timed live: the forward GEMM + online-LSE kernel
-    # (cce_forward = k_fwd + target-logit and merge kernels of a few microseconds)
     fwd_flops = 2.0 * wl.M * wl.V * wl.D
     fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
     bwd_tflops = (n_contr - 1) * fwd_flops / (bwd_ms * 1e-3) / 1e12
-    # the forward runs 256 x 256 tiles with 64-wide K-slices (k_fwd) when D % 64 == 0
-    # and each workgroup runs >= 32 vocab tiles, else 384 x 256 tiles (k_fwd_tall)
-    # when D % 32 == 0 and no block maximum is saved, else k_fwd; the recompute
-    # runs k_recompute_tall when D % 32 == 0 and no tile is skipped
-    n_mt = (wl.M + 255) // 256
-    full = wl.V // 256
-    smax = max(1, min(256 // n_mt, full)) if full > 0 else 1
-    tiles_per_wg = (full + smax - 1) // smax if full > 0 else 0
-    if wl.D % 64 == 0 and tiles_per_wg >= 32:
-        fwd_kernel = "k_fwd"
-    else:
-        fwd_kernel = "k_fwd_tall" if (wl.D % 32 == 0 and not args.block_max) else "k_fwd"
-    rec_kernel = "k_recompute_tall" if (wl.D % 32 == 0 and not feps > 0) else "k_recompute"
-    # the bf16 head with tall recompute tiles runs the pipelined backward: chunk 0's
-    # recompute alone, one fused launch per later chunk (dh / dW of chunk c and the
-    # recompute of c + 1), the last chunk's dh / dW alone
-    bwd_kernels = ("k_recompute_tall + k_bwd_fused + k_grads (cce_backward)"
-                   if rec_kernel == "k_recompute_tall" else f"{rec_kernel} + k_grads (cce_backward)")
-    traffic = None
+
+    # per-kernel figures from the library's launch events over the timed steps
+    kernels = {}
+    if timer is not None:
+        for name, ms, fl in timer.launches():
+            k = kernels.setdefault(name, {"launches": 0, "ms": 0.0, "flops": 0.0})
+            k["launches"] += 1
+            k["ms"] += ms
+            k["flops"] += fl
+        for name, k in kernels.items():
+            k["launches_per_step"] = k["launches"] / args.steps
+            k["avg_launch_us"] = round(k["ms"] / k["launches"] * 1e3, 2)
+            k["share_of_step"] = round(k["ms"] / args.steps / ms_step, 4)
+            k["tflops"] = round(k["flops"] / (k["ms"] * 1e-3) / 1e12, 2) if k["flops"] else None
+            k["flops_per_launch"] = k["flops"] / k["launches"]
+            k["ms"] = round(k["ms"], 3)
+        tsum = sum(k["ms"] for k in kernels.values()) / args.steps
+        print(f"[bench] launches: {sum(k['launches'] for k in kernels.values()) // args.steps} per "
+              f"step, {tsum:.3f} ms of kernel time per step", file=sys.stderr, flush=True)
+        for name, k in sorted(kernels.items(), key=lambda kv: -kv[1]["ms"]):
+            print(f"[bench]   {name:18s} {k['launches_per_step']:5.1f}/step  {k['avg_launch_us']:9.2f} us"
+                  f"  {k['tflops'] or 0:8.1f} TFLOP/s  {100 * k['share_of_step']:5.1f} %",
+                  file=sys.stderr, flush=True)
+    traffic = {}
     if args.traffic_json and os.path.exists(args.traffic_json):
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f)
             if tj.get("workload") == wl.name and tj.get("kernel_source_hash") == B.kernel_source_hash():
-                traffic = tj.get("bytes_per_launch")
+                traffic = {n: e.get("bytes_per_launch") for n, e in tj.get("kernels", {}).items()}
         except Exception:
-            traffic = None
+            traffic = {}
+
+    def roof(name):
+        k = kernels[name]
+        ach = k["flops"] / (k["ms"] * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic.get(name),
+                "avg_launch_us": k["avg_launch_us"], "algorithmic_flops_per_launch": k["flops_per_launch"],
+                "launches_per_step": k["launches_per_step"]}
+
+    gemm = {n: k for n, k in kernels.items() if k["flops"] > 0 and n != "k_target_logit"}
+    dominant = max(gemm, key=lambda n: gemm[n]["ms"]) if gemm else None
+    fwd_kernel = next((n for n in ("k_fwd", "k_fwd_tall") if n in kernels), None)
 
     metric = "fused CCE fwd+bwd tokens/s and % bf16 MFMA peak (8*M*V*D FLOPs)"
     workload = wl.name
@@ -331,6 +427,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_mean": round(ms_total / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -350,19 +447,22 @@ def main():
                      "backward": round(bwd_ms, 4)},
         "workspace_bytes": (B.workspace_bytes_q if quant else B.workspace_bytes)(wl.M, wl.V, wl.D),
         "device_status": status,
-        "roofline": {"kernel": f"cce_forward_q (k_dequant + {fwd_kernel} per chunk)" if quant
-                     else f"{fwd_kernel} (cce_forward)", "bound": "mfma",
-                     "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None if quant else traffic},
-        # the backward's kernels (per vocab chunk: recompute, then dh + dW) timed
-        # together live around cce_backward: 3 contractions of 2*M*V*D FLOPs
-        "roofline_backward": {"kernels": f"k_dequant + {rec_kernel} + k_grads (dh) (cce_backward_q)"
-                              if quant else bwd_kernels,
-                              "bound": "mfma", "achieved": round(bwd_tflops, 2),
-                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        # the dominant kernel (largest share of the step), timed live per launch with the
+        # library's events on the stream it runs on (bench pass 2, the same K steps); FLOPs
+        # per launch as the library counts them (2 per multiply-add at the nominal sizes of
+        # the launch's contractions)
+        "roofline": roof(dominant) if dominant else None,
+        "roofline_forward": roof(fwd_kernel) if fwd_kernel else None,
+        # the whole backward (cce_backward: all of its launches) timed per step
+        "roofline_backward": {"kernels": "cce_backward", "bound": "mfma",
+                              "achieved": round(bwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(bwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "forward_phase_tflops": round(fwd_tflops, 2),
+        "kernels": kernels,
     }
+    if feps > 0 and not quant:
+        result["filter_deviation"] = filter_deviation(head, h, W, y, lse, coef, feps, dh, dW, bwd_ms,
+                                                      args.softcap, bmax, stream)
     del dh, dW
     torch.cuda.empty_cache()
     if args.calibrate_copy:

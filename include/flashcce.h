@@ -239,6 +239,35 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
                           float filter_eps, float block_eps, float* dh,
                           uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Per-launch timing (a profiling hook; no result depends on it).  Between
+ * cce_timing_begin and cce_timing_end, every kernel that a call of this
+ * library enqueues from the calling thread is bracketed by two of the caller's
+ * events, recorded on that call's stream: events[2 i] before launch i and
+ * events[2 i + 1] after it, with kinds[i] = the kernel (cce_kernel_name gives
+ * its name) and flops[i] = the launch's algorithmic floating-point operations
+ * (2 per multiply-add of the contractions it performs, counted at their
+ * nominal sizes: M rows, the vocabulary entries the launch covers, D; 0 for a
+ * kernel without a contraction), for the first `capacity` launches of the
+ * window (later launches are not bracketed).  The time of launch i is the
+ * elapsed time between its two events once the stream has completed them.
+ *   events    2 * capacity hipEvent_t handles (host array of device events,
+ *             created by the caller with timing enabled; none may be NULL)
+ *   kinds     capacity int32 (host array)
+ *   flops     capacity doubles (host array), or NULL
+ *   capacity  >= 1, else CCE_EINVAL.  The window belongs to the calling
+ *             thread; a new begin replaces an open window.
+ * cce_timing_end closes the window and returns the number of launches
+ * bracketed, or -1 if no window was open or an event could not be recorded.
+ * Recording events between launches adds a few microseconds per launch.
+ */
+cce_status cce_timing_begin(void* const* events, int32_t* kinds, double* flops,
+                            int32_t capacity);
+int32_t cce_timing_end(void);
+
+/* Name of a kernel kind reported by the timing hook (static string). */
+const char* cce_kernel_name(int32_t kind);
+
 #ifdef __cplusplus
 }
 #endif

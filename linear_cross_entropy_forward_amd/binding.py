@@ -41,6 +41,9 @@ SIGNATURES = {
                              _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "cce_backward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i64,
                               _c_i64, _c_i64, _c_f, _c_f, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_timing_begin": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_int32]),
+    "cce_timing_end": (ctypes.c_int32, []),
+    "cce_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
 _lib = None
@@ -284,6 +287,47 @@ class Head:
 
     def clear_status(self):
         self.status.zero_()
+
+
+class LaunchTimer:
+    """Per-launch timing through the library's profiling hook: within
+    ``with timer:`` every kernel the library enqueues from this thread is
+    bracketed by two events (recorded on the call's stream).  After the stream
+    has completed, ``launches()`` gives (kernel name, milliseconds, algorithmic
+    FLOPs) per launch.
+    Holds `capacity` launches; later ones are not bracketed."""
+
+    def __init__(self, capacity: int = 256):
+        self.capacity = int(capacity)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * self.capacity)]
+        # torch creates an event's HIP handle on its first record
+        st = torch.cuda.current_stream()
+        for e in self.events:
+            e.record(st)
+        torch.cuda.synchronize()
+        self._handles = (ctypes.c_void_p * (2 * self.capacity))(*[e.cuda_event for e in self.events])
+        self._kinds = (ctypes.c_int32 * self.capacity)()
+        self._flops = (ctypes.c_double * self.capacity)()
+        self.n = 0
+
+    def __enter__(self):
+        _check("cce_timing_begin", load().cce_timing_begin(self._handles, self._kinds, self._flops,
+                                                           self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        n = int(load().cce_timing_end())
+        if n < 0 and exc[0] is None:
+            raise RuntimeError("cce_timing_end: the timing window failed to record its events")
+        self.n = max(n, 0)
+        return False
+
+    def launches(self):
+        """[(kernel name, milliseconds, algorithmic FLOPs)] per bracketed launch."""
+        lib = load()
+        return [(lib.cce_kernel_name(int(self._kinds[i])).decode(),
+                 self.events[2 * i].elapsed_time(self.events[2 * i + 1]), float(self._flops[i]))
+                for i in range(self.n)]
 
 
 def to_device_bits(bits, device) -> torch.Tensor:

@@ -38,6 +38,8 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
   size_t part_m, part_s, tgt, pairs, g, flags;
+  size_t epi_rec, epi_nruns, epi_first, epi_last, epi_end;  // the epilogue's row-pass state
+  size_t tc, skey[2], sval[2], shist, tF, tL;  // the backward's exact onehot part
   size_t g2;  // the second gradient buffer of the pipelined backward (0: none)
   size_t psplit;  // split-K partial tiles of dh (psplit_tiles of 256 x 256 fp32)
   long long psplit_tiles;
@@ -77,6 +79,22 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.part_s = take((size_t)Scap * L.Mpad * sizeof(float));
   L.tgt = take((size_t)L.Mpad * sizeof(float));
   L.pairs = take((size_t)L.Mpad * cce::kPairStride * sizeof(double));
+  {
+    const int64_t nblk = (M + cce::kEpiRows - 1) / cce::kEpiRows;
+    L.epi_rec = take((size_t)nblk * cce::kEpiRows * cce::kEpiRecBytes);
+    L.epi_nruns = take((size_t)nblk * sizeof(int));
+    L.epi_first = take((size_t)L.Mpad * sizeof(int));
+    L.epi_last = take((size_t)L.Mpad * sizeof(int));
+    L.epi_end = off;
+  }
+  L.tc = take((size_t)L.Mpad * sizeof(float));
+  for (int q = 0; q < 2; ++q) {
+    L.skey[q] = take((size_t)L.Mpad * sizeof(int));
+    L.sval[q] = take((size_t)L.Mpad * sizeof(int));
+  }
+  L.shist = take((size_t)256 * ((M + 2047) / 2048) * sizeof(int));
+  L.tF = take((size_t)((M + 63) / 64) * D * sizeof(float));
+  L.tL = take((size_t)((M + 63) / 64) * D * sizeof(float));
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   const size_t base = off;
@@ -118,11 +136,89 @@ cce_status device_ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+void set_target_regions(cce::BwdArgs& a, const Layout& L, char* base) {
+  a.tc = reinterpret_cast<float*>(base + L.tc);
+  for (int q = 0; q < 2; ++q) {
+    a.skey[q] = reinterpret_cast<int*>(base + L.skey[q]);
+    a.sval[q] = reinterpret_cast<int*>(base + L.sval[q]);
+  }
+  a.shist = reinterpret_cast<int*>(base + L.shist);
+  a.tF = reinterpret_cast<float*>(base + L.tF);
+  a.tL = reinterpret_cast<float*>(base + L.tL);
+}
+
+// The calling thread's timing window (cce_timing_begin .. cce_timing_end).
+struct TimingLog {
+  void* const* ev;  // 2 * cap caller-owned events: before / after launch i
+  int32_t* kinds;   // cap entries
+  double* flops;    // cap entries, or null
+  int32_t cap, n;
+  bool on, failed;
+};
+thread_local TimingLog g_tlog{};
+
 }  // namespace
+
+namespace cce {
+void timing_pre(hipStream_t st) {
+  TimingLog& t = g_tlog;
+  if (!t.on || t.n >= t.cap) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(t.ev[2 * t.n]), st) != hipSuccess) t.failed = true;
+}
+void timing_post(int kind, double flops, hipStream_t st) {
+  TimingLog& t = g_tlog;
+  if (!t.on || t.n >= t.cap) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(t.ev[2 * t.n + 1]), st) != hipSuccess) t.failed = true;
+  if (t.flops) t.flops[t.n] = flops;
+  t.kinds[t.n++] = kind;
+}
+}  // namespace cce
 
 extern "C" {
 
-int cce_abi_version(void) { return 5; }
+int cce_abi_version(void) { return 6; }
+
+cce_status cce_timing_begin(void* const* events, int32_t* kinds, double* flops,
+                            int32_t capacity) {
+  if (!events || !kinds || capacity < 1) return CCE_EINVAL;
+  for (int32_t i = 0; i < 2 * capacity; ++i)
+    if (!events[i]) return CCE_EINVAL;
+  g_tlog = TimingLog{events, kinds, flops, capacity, 0, true, false};
+  return CCE_OK;
+}
+
+int32_t cce_timing_end(void) {
+  TimingLog& t = g_tlog;
+  const int32_t n = t.on && !t.failed ? t.n : -1;
+  t = TimingLog{};
+  return n;
+}
+
+const char* cce_kernel_name(int32_t kind) {
+  switch (kind) {
+    case cce::KN_FWD: return "k_fwd";
+    case cce::KN_FWD_TALL: return "k_fwd_tall";
+    case cce::KN_TARGET_LOGIT: return "k_target_logit";
+    case cce::KN_FWD_MERGE: return "k_fwd_merge";
+    case cce::KN_EPI_BLOCKS: return "k_epi_blocks";
+    case cce::KN_EPI_PAIRS: return "k_epi_pairs";
+    case cce::KN_EPI_FINAL: return "k_epi_final";
+    case cce::KN_EPI_COEF: return "k_epi_coef";
+    case cce::KN_EPI_INIT: return "k_epi_init";
+    case cce::KN_RECOMPUTE: return "k_recompute";
+    case cce::KN_RECOMPUTE_TALL: return "k_recompute_tall";
+    case cce::KN_BWD_FUSED: return "k_bwd_fused";
+    case cce::KN_GRADS: return "k_grads";
+    case cce::KN_SPLIT_REDUCE: return "k_split_reduce";
+    case cce::KN_DEQUANT: return "k_dequant";
+    case cce::KN_TARGET_LOGIT_Q: return "k_target_logit_q";
+    case cce::KN_FWD_FOLD: return "k_fwd_fold";
+    case cce::KN_TARGET_DH: return "k_target_dh";
+    case cce::KN_SORT: return "k_sort";
+    case cce::KN_TARGET_DW: return "k_target_dw";
+    default: return "unknown";
+  }
+}
 
 const char* cce_status_string(int status) {
   switch (status) {
@@ -196,8 +292,7 @@ static cce_status epilogue_common(const float* logp, const int32_t* y, const int
   if (M < 1 || M > kMaxM || n_pairs < 1 || (int64_t)n_pairs > M) return CCE_ESHAPE;
   // the epilogue's part of the workspace depends on M only; any V, D >= 1 give it
   const Layout L = layout(M, 1, 1);
-  if (ws_bytes < L.pairs + (size_t)L.Mpad * cce::kPairStride * sizeof(double) ||
-      (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+  if (ws_bytes < L.epi_end || (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
     return CCE_EWORKSPACE;
   const cce_status ds = device_ok();
   if (ds != CCE_OK) return ds;
@@ -213,7 +308,12 @@ static cce_status epilogue_common(const float* logp, const int32_t* y, const int
   a.beta = (double)beta;
   a.gamma = (double)gamma;
   a.scope = scope;
-  a.pairs = reinterpret_cast<double*>(static_cast<char*>(ws) + L.pairs);
+  char* base = static_cast<char*>(ws);
+  a.pairs = reinterpret_cast<double*>(base + L.pairs);
+  a.rec = base + L.epi_rec;
+  a.nruns = reinterpret_cast<int*>(base + L.epi_nruns);
+  a.first = reinterpret_cast<int*>(base + L.epi_first);
+  a.last = reinterpret_cast<int*>(base + L.epi_last);
   a.out5 = out5;
   a.pair_stats = pair_stats;
   a.coef = coef;
@@ -280,6 +380,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit);
   a.P_tiles = L.psplit_tiles;
+  set_target_regions(a, L, base);
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
 }
@@ -378,6 +479,7 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit_q);
   a.P_tiles = L.psplit_tiles_q;
+  set_target_regions(a, L, base);
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
   a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);

@@ -37,7 +37,8 @@
 
 namespace cce {
 
-// The gradient entries of one recomputed tile, straight from the accumulators
+// The gradient entries of one recomputed tile, coef * softmax (times sech^2
+// under a cap; the onehot part is not in G), straight from the accumulators
 // to G: per (ii, jj, q) a lane holds 4 consecutive vocab entries of one token
 // (vocab block wi*4 + ii of the tile, entries 8q + 4*half .. +3 of the row); the
 // lanes l and l + 32 of a token trade halves with v_permlane32_swap so that
@@ -80,9 +81,11 @@ __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
             p = fast_exp2(fmaf(acc[ii][jj][4 * q + e], LOG2E, nlse[jj]));
             if (vbad) p = 0.f;
           }
-          const bool is_t = TGT && (off[jj] == ii * 32 + 8 * q + e);
+          // the target's entry is kept from the filter; its onehot part (-coef
+          // sech^2) is applied outside these tiles, exactly
+          const bool is_t = FILTER && TGT && (off[jj] == ii * 32 + 8 * q + e);
           if (FILTER && p < filter_eps && !is_t) p = 0.f;
-          g[e] = cf[jj] * (is_t ? p - 1.f : p) * sech2;
+          g[e] = cf[jj] * p * sech2;
         }
         pk[q][0] = pack_bf16x2(g[0], g[1]);
         pk[q][1] = pack_bf16x2(g[2], g[3]);
@@ -684,9 +687,10 @@ static void grads_probs(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* 
   const int nT = a.nMt * nDt;
   const int dh_nl =
       sp.ks == 1 ? pad8(nT) : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
+  // dh accumulates into what launch_target_dh wrote (the onehot part)
   dh = GemmProb{OpRef{G, 0, 0, 0}, OpRef{Wc, a.D, vlen, a.D}, (size_t)nkbV * 8192,
                 (size_t)kTile, nvt * kTile, a.dh, a.D, a.M, a.D, a.nMt, nDt, dh_nl, a.flags,
-                fstride, 1, v0 == 0 ? 0 : 1, sp.ks, sp.n_full, a.P, 0};
+                fstride, 1, 1, sp.ks, sp.n_full, a.P, 0};
   dw = GemmProb{OpRef{G, nkbV, 0, 0}, OpRef{a.H, a.D, a.M, a.D}, (size_t)8 * 8192,
                 (size_t)kTile, a.Mpad, a.dW ? a.dW + (size_t)v0 * a.D : nullptr, a.D, vlen,
                 a.D, nvt, nDt, pad8(nvt * nDt), a.flags, 1, fstride, 0, 1, nvt * nDt, nullptr, 0};
@@ -711,7 +715,9 @@ static RecArgs rec_args(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* 
 static hipError_t split_reduce(const GemmProb& dh, const DhSplit& sp, hipStream_t st) {
   const int nT = dh.nA * dh.nB;
   if (sp.n_full < nT)
-    hipLaunchKernelGGL(k_split_reduce, dim3(nT - sp.n_full, TILE / 16), dim3(256), 0, st, dh);
+    CCE_TIMED(KN_SPLIT_REDUCE, 0.0, st,
+              hipLaunchKernelGGL(k_split_reduce, dim3(nT - sp.n_full, TILE / 16), dim3(256), 0, st,
+                                 dh));
   return hipGetLastError();
 }
 
@@ -733,6 +739,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     chunks.emplace_back(v0, vlen);
   }
   const int nch = (int)chunks.size();
+  if ((e = launch_target_dh(a, st)) != hipSuccess) return e;
+  const bool with_dw_all = a.q.Wq == nullptr;
 
   // Pipelined form (bf16 head, tall recompute, a second gradient buffer):
   // recompute chunk 0, then one launch per chunk c running c's dh / dW tasks
@@ -744,7 +752,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     u16* const Gb[2] = {a.G, a.G2};
     {
       const RecArgs r = rec_args(a, 0, chunks[0].second, a.W, Gb[0]);
-#define CCE_REC(FILT, CAP) hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r)
+#define CCE_REC(FILT, CAP)                                                                    \
+  CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
       if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
       else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
 #undef CCE_REC
@@ -762,17 +772,21 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
         const int v1 = chunks[c + 1].first;
         const RecArgs r = rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]);
         const dim3 grid(dh.nl + dw.nl + r.nl);
-#define CCE_FUSED(FILT, CAP) hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r)
+#define CCE_FUSED(FILT, CAP)                                                                  \
+  CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * (2.0 * vlen + r.vlen), st,                        \
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r))
         if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
         else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
 #undef CCE_FUSED
       } else {
-        hipLaunchKernelGGL((k_grads<false, true>), dim3(dh.nl + dw.nl), dim3(NT), 0, st, dh, dw);
+        CCE_TIMED(KN_GRADS, 4.0 * a.M * a.D * vlen, st,
+                  hipLaunchKernelGGL((k_grads<false, true>), dim3(dh.nl + dw.nl), dim3(NT), 0, st,
+                                     dh, dw));
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
     }
-    return hipSuccess;
+    return launch_target_dw(a, st);
   }
 
   for (int c = 0; c < nch; ++c) {
@@ -787,7 +801,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     // 1. recompute + gradient tile
     if (tall) {
       const RecArgs r = rec_args(a, v0, vlen, Wc, a.G);
-#define CCE_REC(FILT, CAP) hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r)
+#define CCE_REC(FILT, CAP)                                                                    \
+  CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
       if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
       else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
 #undef CCE_REC
@@ -795,9 +811,10 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     } else {
       const int n = pad8(a.nMt * nvt);
 #define CCE_RECOMPUTE(VEC, FILT, KT, CAP)                                                          \
-  hipLaunchKernelGGL((k_recompute<VEC, FILT, KT, CAP>), dim3(n), dim3(NT), 0, st, a.H, Wc, a.y,    \
-                     a.lse, a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, a.softcap, a.filter_eps,       \
-                     a.block_eps, a.G, a.flags, nkbV, bmc)
+  CCE_TIMED(KN_RECOMPUTE, 2.0 * a.M * a.D * vlen, st,                                              \
+            hipLaunchKernelGGL((k_recompute<VEC, FILT, KT, CAP>), dim3(n), dim3(NT), 0, st, a.H,   \
+                               Wc, a.y, a.lse, a.coef, a.M, a.D, v0, vlen, a.nMt, nvt, a.softcap,  \
+                               a.filter_eps, a.block_eps, a.G, a.flags, nkbV, bmc))
 #define CCE_RECOMPUTE_F(VEC, KT, CAP)                                                              \
   do {                                                                                             \
     if (filt) CCE_RECOMPUTE(VEC, true, KT, CAP); else CCE_RECOMPUTE(VEC, false, KT, CAP);          \
@@ -825,18 +842,20 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       grads_probs(a, v0, vlen, Wc, a.G, dh, dw, sp);
       // the quantised head is frozen: dh only
       const dim3 grid(with_dw ? dh.nl + dw.nl : dh.nl);
+#define CCE_GRADS(SKIP, VEC)                                                                  \
+  CCE_TIMED(KN_GRADS, (with_dw ? 4.0 : 2.0) * a.M * a.D * vlen, st,                            \
+            hipLaunchKernelGGL((k_grads<SKIP, VEC>), grid, dim3(NT), 0, st, dh, dw))
       if (a.vec) {
-        if (skip) hipLaunchKernelGGL((k_grads<true, true>), grid, dim3(NT), 0, st, dh, dw);
-        else hipLaunchKernelGGL((k_grads<false, true>), grid, dim3(NT), 0, st, dh, dw);
+        if (skip) CCE_GRADS(true, true); else CCE_GRADS(false, true);
       } else {
-        if (skip) hipLaunchKernelGGL((k_grads<true, false>), grid, dim3(NT), 0, st, dh, dw);
-        else hipLaunchKernelGGL((k_grads<false, false>), grid, dim3(NT), 0, st, dh, dw);
+        if (skip) CCE_GRADS(true, false); else CCE_GRADS(false, false);
       }
+#undef CCE_GRADS
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
     }
   }
-  return hipSuccess;
+  return with_dw_all ? launch_target_dw(a, st) : hipSuccess;
 }
 
 }  // namespace cce

@@ -804,18 +804,24 @@ __device__ __forceinline__ void tall_mfma(const FragsTall& f, int q, AccTall& ac
 
 // Direct-to-LDS loads of one K-slice of a transposed blocked operand (OP_KBLK)
 // 384 columns wide (the dW contraction's A = G^T over a tall vocabulary tile):
-// 32 k-rows of 768 bytes (48 16-byte chunks).  Lane L of instruction p (0..5)
-// of wave w fills LDS chunk g = 64 (6 w + p) + L, i.e. k-row g / 48 at position
-// g % 48, with the global chunk (g % 48) ^ kswz(k-row) (the swizzle of the K
-// forms; it changes only the low 4 bits, so chunks stay inside the row).
-// Chunk c of k-row kr is 8 columns of block c / 4: byte (c / 4) 16384 + 64 kr +
-// 16 (c % 4) from the slice's base.  Blocks at or past nvb (the tile's valid
-// 32-column blocks) read as zero: the resource ends there.
+// the slice (32 k-rows = tokens, 12 blocks of 32 columns = vocabulary) is 12
+// pieces of 2 KB, one per block (32 k-rows x 64 bytes, contiguous in G), and
+// lands in LDS in the same order: block b's k-row kr at b * 2048 + kr * 64.
+// Each load instruction copies 1 KB contiguous (16 k-rows of one block):
+// instruction q = 6 w + p (wave w, p = 0..5) takes block q / 2, k-rows
+// 16 (q % 2) .. +15.  Within a 64-byte k-row the 16-byte chunk c sits at
+// position c ^ swzk(kr) (swzk(kr) = 2 ((kr >> 1) & 1)): the transposing
+// fragment read takes 4 consecutive k-rows x 32 bytes per 16 lanes, and with
+// this XOR those pieces fall in distinct banks for 32 or 64 banks of 4 bytes.
+// Blocks at or past nvb (the tile's valid 32-column blocks) read as zero: the
+// resource ends there.
+__device__ __forceinline__ int swzk(int kr) { return ((kr >> 1) & 1) << 1; }
+
 struct DmaKblkTall {
   const u16* base;
-  int ld;   // blocks per 256-row tile of X
-  int nvb;  // valid blocks of this tile (1..12)
-  int voff[6];
+  int ld;    // blocks per 256-row tile of X
+  int nvb;   // valid blocks of this tile (1..12)
+  int voff;  // this lane's byte offset: its chunk of wave w's first 1 KB piece
   unsigned ldsw;
   struct Slice {
     i32x4 rs;
@@ -826,13 +832,8 @@ struct DmaKblkTall {
     const int nb = (op.cols + 31) >> 5;
     nvb = nb < 12 ? nb : 12;
     ldsw = (unsigned)__builtin_amdgcn_readfirstlane(w * 6144);
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      const int g = 64 * (6 * w + p) + lane;
-      const int kr = g / 48;
-      const int c = (g % 48) ^ kswz(kr);
-      voff[p] = (c >> 2) * 16384 + kr * 64 + (c & 3) * 16;
-    }
+    const int kr = lane >> 2;  // k-row within the 16 of one instruction (kr and kr + 16 share swzk)
+    voff = 3 * w * 16384 + kr * 64 + (((lane & 3) ^ swzk(kr)) << 4);
   }
   __device__ __forceinline__ Slice slice(int k0) const {
     Slice sl;
@@ -840,8 +841,9 @@ struct DmaKblkTall {
     sl.rs = make_rsrc(sb, (unsigned)nvb * 16384u);
     return sl;
   }
+  // instruction p of this wave: block 3 w + p / 2, k-rows 16 (p % 2) ..
   __device__ __forceinline__ void issue(const Slice& sl, unsigned dst, int p) const {
-    dma16(sl.rs, voff[p], dst + ldsw + p * 1024, 0);
+    dma16(sl.rs, voff + (p >> 1) * 16384 + (p & 1) * 1024, dst + ldsw + p * 1024, 0);
   }
   __device__ __forceinline__ void issue_all(int k0, unsigned dst) const {
     const Slice sl = slice(k0);
@@ -850,23 +852,23 @@ struct DmaKblkTall {
   }
 };
 
-// Fragment offsets of the K forms in a tall stage: A (768-byte k-rows, the
-// 384 columns of DmaKblkTall) per MFMA tile t, and B (512-byte k-rows, a K-form
-// operand of 256 columns after the A region; tile j at b ^ (j << 6)).  The
-// transposing read as in FragAddr: in each 16-lane group, lane s points at
-// k-row kr0 + s/4 and column i0 + 4 (s % 4); two reads 4 k-rows apart give the
-// lane's 8 K elements; lanes 16..31 take i0 + 16, lanes 32..63 K elements
-// 8..15 (k-rows + 8).  Sub-step 1 is 16 k-rows further.
+// Fragment offsets of the K forms in a tall stage: A (the block-major G^T slice
+// of DmaKblkTall; MFMA tile t of wave wi is block 6 wi + t) and B (512-byte
+// k-rows, a K-form operand of 256 columns after the A region; tile j at
+// b ^ (j << 6)).  The transposing read as in FragAddr: in each 16-lane group,
+// lane s points at k-row kr0 + s/4 and column i0 + 4 (s % 4); two reads 4
+// k-rows apart give the lane's 8 K elements; lanes 16..31 take i0 + 16, lanes
+// 32..63 K elements 8..15 (k-rows + 8).  In A the second read is 256 bytes on,
+// tile t at + t * 2048, and sub-step 1 (16 k-rows further) at + 1024 (swzk is
+// the same for k-rows 4, 8 and 16 apart).
 struct FragAddrKTall {
-  int a[6];
+  int a;  // tile 0, sub-step 0, first read
   int b;
   __device__ __forceinline__ void init(int lane, int wi, int wj) {
     const int s = lane & 15, gi = (lane >> 4) & 1, half = lane >> 5;
     const int kr = 8 * half + (s >> 2);
     const int c0 = 2 * gi + ((s >> 1) & 1);
-#pragma unroll
-    for (int t = 0; t < 6; ++t)
-      a[t] = kr * 768 + (((24 * wi + 4 * t + c0) ^ kswz(kr)) << 4) + 8 * (s & 1);
+    a = wi * 6 * 2048 + kr * 64 + ((c0 ^ swzk(kr)) << 4) + 8 * (s & 1);
     b = TALL_A_BYTES + kr * 512 + ((c0 ^ kswz(kr)) << 4) + 8 * (s & 1) + wj * 256;
   }
 };
@@ -881,9 +883,9 @@ __device__ __forceinline__ bf16x8 read_tr_frag_w(const unsigned char* p, int sec
 // Fragment r (0..9) of a K-form tall sub-step, in the consuming order A0, B0..B3, A1..A5.
 __device__ __forceinline__ void tall_read_frag(const unsigned char* stage, const FragAddrKTall& fa,
                                                int sub, int r, FragsTall& f) {
-  if (r == 0) f.a[0] = read_tr_frag_w(stage + fa.a[0] + sub * 12288, 3072);
+  if (r == 0) f.a[0] = read_tr_frag_w(stage + fa.a + sub * 1024, 256);
   else if (r < 5) f.b[r - 1] = read_tr_frag(stage + ((fa.b ^ ((r - 1) << 6)) + sub * 8192));
-  else f.a[r - 4] = read_tr_frag_w(stage + fa.a[r - 4] + sub * 12288, 3072);
+  else f.a[r - 4] = read_tr_frag_w(stage + fa.a + (r - 4) * 2048 + sub * 1024, 256);
 }
 
 // Operand forms of a tall tile: row-major A and B (the forward and the

@@ -18,8 +18,12 @@
 // max(0, -s) (hinge, derivative 0 at the kink), and
 //   L = mean_b (nll_weight NLL_b + lambda P_b).
 //
-// Three small kernels: per-pair sums (one workgroup per pair, fixed-order fp64
-// tree reduction), batch means (one workgroup), per-row coefficients.
+// Each row is read once: a row pass records per-run partial sums (fp64, fixed
+// order) for blocks of rows, a pair pass combines each pair's records in block
+// order and forms its terms, then the batch means (one workgroup) and the
+// per-row coefficients.  Every sum has a fixed order, so results are
+// deterministic; the cost is linear in the rows plus the pairs (for pairs
+// whose rows are contiguous, the usual layout).
 #include <math.h>
 
 #include "cce_launch.hpp"
@@ -46,67 +50,182 @@ __device__ double sigmoid_d(double x) {
   return e / (1.0 + e);
 }
 
-__global__ __launch_bounds__(256) void k_epi_pairs(const float* __restrict__ logp,
-                                                   const int* __restrict__ y,
-                                                   const int* __restrict__ seg, int M, int B,
+// Row pass: block k holds rows [kR, kR + R) (R = kEpiRows).  A run is a
+// maximal range of consecutive rows of the block with the same pair index; each
+// run gets one record (pair, per-kind fp64 sums and counts), written at
+// rec[kR + j] for the block's j-th run, with nruns[k] = the block's run count.
+// One wave reduces one run at a time (lane l takes rows s + l, s + l + 64, ...
+// in order, then a fixed shuffle tree), so every sum has a fixed order.  Rows
+// with an invalid pair index take part in no run's sums (status bit).  Each
+// pair's first and last block are kept with integer atomic min / max
+// (order-independent values).
+struct EpiRec {
+  int pair, nc, nr, np;
+  double sc, sr, sp, pad;
+};
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_epi_init(int B, int* __restrict__ first,
+                                                  int* __restrict__ last) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < B) {
+    first[b] = 0x7fffffff;
+    last[b] = -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_epi_blocks(const float* __restrict__ logp,
+                                                    const int* __restrict__ y,
+                                                    const int* __restrict__ seg, int M, int B,
+                                                    EpiRec* __restrict__ rec,
+                                                    int* __restrict__ nruns,
+                                                    int* __restrict__ first,
+                                                    int* __restrict__ last, unsigned* status) {
+  __shared__ int start[kEpiRows + 1];  // row offsets of the block's run starts (+ end)
+  __shared__ int wcnt[4], wbase[4];
+  const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r0 = k * kEpiRows, nrow = min(kEpiRows, M - r0);
+  constexpr int PER = kEpiRows / 256;  // consecutive rows per thread
+  // 1. status checks and run starts; thread t owns rows PER t .. PER t + PER - 1
+  int pr[PER + 1];
+  unsigned err = 0u;
+  pr[0] = -2;
+  const int t0 = PER * tid;
+  if (t0 > 0 && t0 - 1 < nrow) {
+    const int p = seg[r0 + t0 - 1] >> 2;
+    pr[0] = (p >= 0 && p < B) ? p : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int r = t0 + u;
+    pr[u + 1] = -3;
+    if (r < nrow) {
+      const int sg = seg[r0 + r];
+      const int kind = sg & 3, p = sg >> 2;
+      const bool ok = p >= 0 && p < B;
+      if (!ok) err |= 2u;                            // CCE_DERR_PAIR
+      if (kind != 0 && y[r0 + r] < 0) err |= 1u;     // CCE_DERR_TARGET
+      pr[u + 1] = ok ? p : -1;
+    }
+  }
+  if (err) atomicOr(status, err);
+  int mystarts = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (t0 + u < nrow && (t0 + u == 0 || pr[u + 1] != pr[u])) ++mystarts;
+  // 2. exclusive prefix of the start counts in thread order (wave scan, then waves)
+  int incl = mystarts;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wcnt[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int q = 0; q < 4; ++q) {
+      wbase[q] = acc;
+      acc += wcnt[q];
+    }
+    start[kEpiRows] = acc;  // the block's run count, parked here for a moment
+  }
+  __syncthreads();
+  int at = wbase[w] + incl - mystarts;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (t0 + u < nrow && (t0 + u == 0 || pr[u + 1] != pr[u])) start[at++] = t0 + u;
+  __syncthreads();
+  const int nr = start[kEpiRows];
+  __syncthreads();
+  if (tid == 0) {
+    start[nr] = nrow;
+    nruns[k] = nr;
+  }
+  __syncthreads();
+  // 3. one wave per run, runs w, w + 4, ...
+  for (int j = w; j < nr; j += 4) {
+    const int s = start[j], e = start[j + 1];
+    const int p0 = seg[r0 + s] >> 2;
+    const int p = (p0 >= 0 && p0 < B) ? p0 : -1;
+    double sc = 0, sr = 0, sp = 0;
+    int nc = 0, nrr = 0, np = 0;
+    if (p >= 0) {
+      for (int r = s + lane; r < e; r += 64) {
+        const int kind = seg[r0 + r] & 3;
+        const double lp = (double)logp[r0 + r];
+        if (kind == 2) { sc += lp; ++nc; }
+        else if (kind == 3) { sr += lp; ++nrr; }
+        else if (kind == 1) { sp += lp; ++np; }
+      }
+    }
+    sc = wave_sum_d(sc);
+    sr = wave_sum_d(sr);
+    sp = wave_sum_d(sp);
+    nc = wave_sum_i(nc);
+    nrr = wave_sum_i(nrr);
+    np = wave_sum_i(np);
+    if (lane == 0) {
+      EpiRec& R = rec[(size_t)r0 + j];
+      R.pair = p;
+      R.nc = nc;
+      R.nr = nrr;
+      R.np = np;
+      R.sc = sc;
+      R.sr = sr;
+      R.sp = sp;
+      R.pad = 0.0;
+      if (p >= 0) {
+        atomicMin(first + p, k);
+        atomicMax(last + p, k);
+      }
+    }
+  }
+}
+
+// Pair pass: one wave per pair b gathers the records of b from its first to
+// its last block, in (block, run) order, then forms the pair's objective and
+// coefficients.
+__global__ __launch_bounds__(256) void k_epi_pairs(const EpiRec* __restrict__ rec,
+                                                   const int* __restrict__ nruns,
+                                                   const int* __restrict__ first,
+                                                   const int* __restrict__ last, int B,
                                                    int objective, double nll_weight,
                                                    double lambda, double beta, double gamma,
                                                    int scope, double* __restrict__ pairs,
                                                    unsigned* status) {
-  __shared__ double sh[3][256];
-  __shared__ int shn[3][256];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;
   double sc = 0, sr = 0, sp = 0;
   int nc = 0, nr = 0, np = 0;
-  unsigned err = 0u;
-  // Thread tid visits rows tid, tid + 256, tid + 512, ... in that order; the
-  // loads of 8 of them are issued together so the scan is not one memory
-  // latency per row.
-  constexpr int U = 8;
-  for (int base = 0; base < M; base += 256 * U) {
-    int sv[U], yv[U];
-    float lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * 256 + tid;
-      const bool in = i < M;
-      sv[u] = in ? seg[i] : -4;  // pair -1: matches no pair, checked by nobody
-      lv[u] = in ? logp[i] : 0.f;
-      yv[u] = (in && b == 0) ? y[i] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (base + u * 256 + tid >= M) continue;
-      const int s = sv[u];
-      const int kind = s & 3, pr = s >> 2;
-      if (b == 0) {
-        if (pr < 0 || pr >= B) err |= 2u;                       // CCE_DERR_PAIR
-        if (kind != 0 && yv[u] < 0) err |= 1u;                  // CCE_DERR_TARGET
-      }
-      if (pr != b) continue;
-      const double lp = (double)lv[u];
-      if (kind == 2) { sc += lp; ++nc; }
-      else if (kind == 3) { sr += lp; ++nr; }
-      else if (kind == 1) { sp += lp; ++np; }
-    }
-  }
-  if (err) atomicOr(status, err);
-  sh[0][tid] = sc; sh[1][tid] = sr; sh[2][tid] = sp;
-  shn[0][tid] = nc; shn[1][tid] = nr; shn[2][tid] = np;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) {
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        sh[q][tid] += sh[q][tid + off];
-        shn[q][tid] += shn[q][tid + off];
+  const int k1 = last[b];
+  for (int k = first[b]; k <= k1; ++k) {
+    const int n = nruns[k];
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const bool hit = j < n && rec[(size_t)k * kEpiRows + j].pair == b;
+      unsigned long long m = __ballot(hit);
+      while (m) {  // the matching records in order (uniform across the wave)
+        const int jj = j0 + __builtin_ctzll(m);
+        m &= m - 1ull;
+        const EpiRec& R = rec[(size_t)k * kEpiRows + jj];
+        sc += R.sc; sr += R.sr; sp += R.sp;
+        nc += R.nc; nr += R.nr; np += R.np;
       }
     }
-    __syncthreads();
   }
-  if (tid != 0) return;
-  sc = sh[0][0]; sr = sh[1][0]; sp = sh[2][0];
-  nc = shn[0][0]; nr = shn[1][0]; np = shn[2][0];
+  if (lane != 0) return;
   double* P = pairs + (size_t)b * kPairStride;
   if (nc == 0 || nr == 0) {
     atomicOr(status, 4u);  // CCE_DERR_EMPTY_SPAN
@@ -213,17 +332,30 @@ __global__ __launch_bounds__(256) void k_epi_coef(const int* __restrict__ seg,
 }
 
 hipError_t launch_epilogue(const EpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_epi_pairs, dim3(a.n_pairs), dim3(256), 0, st, a.logp, a.y, a.seg, a.M,
-                     a.n_pairs, a.objective, a.nll_weight, a.lambda, a.beta, a.gamma, a.scope,
-                     a.pairs, a.status);
+  const int nblk = (a.M + kEpiRows - 1) / kEpiRows;
+  CCE_TIMED(KN_EPI_INIT, 0.0, st,
+            hipLaunchKernelGGL(k_epi_init, dim3((a.n_pairs + 255) / 256), dim3(256), 0, st,
+                               a.n_pairs, a.first, a.last));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_epi_final, dim3(1), dim3(256), 0, st, a.pairs, a.n_pairs, a.nll_weight,
-                     a.lambda, a.out5, a.pair_stats, a.status);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_epi_coef, dim3((a.M + 255) / 256), dim3(256), 0, st, a.seg, a.pairs, a.M,
-                     a.n_pairs, a.coef);
+  CCE_TIMED(KN_EPI_BLOCKS, 0.0, st,
+            hipLaunchKernelGGL(k_epi_blocks, dim3(nblk), dim3(256), 0, st, a.logp, a.y, a.seg,
+                               a.M, a.n_pairs, reinterpret_cast<EpiRec*>(a.rec), a.nruns, a.first,
+                               a.last, a.status));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  CCE_TIMED(KN_EPI_PAIRS, 0.0, st,
+            hipLaunchKernelGGL(k_epi_pairs, dim3((a.n_pairs + 3) / 4), dim3(256), 0, st,
+                               reinterpret_cast<const EpiRec*>(a.rec), a.nruns, a.first, a.last,
+                               a.n_pairs, a.objective, a.nll_weight, a.lambda, a.beta, a.gamma,
+                               a.scope, a.pairs, a.status));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  CCE_TIMED(KN_EPI_FINAL, 0.0, st,
+            hipLaunchKernelGGL(k_epi_final, dim3(1), dim3(256), 0, st, a.pairs, a.n_pairs,
+                               a.nll_weight, a.lambda, a.out5, a.pair_stats, a.status));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  CCE_TIMED(KN_EPI_COEF, 0.0, st,
+            hipLaunchKernelGGL(k_epi_coef, dim3((a.M + 255) / 256), dim3(256), 0, st, a.seg,
+                               a.pairs, a.M, a.n_pairs, a.coef));
   return hipGetLastError();
 }
 

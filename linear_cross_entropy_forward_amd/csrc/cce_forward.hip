@@ -411,11 +411,13 @@ template <bool TAIL>
 static void launch_fwd_tiles(const FwdArgs& a, int S, int T, int t0, int t1, int slot0,
                              hipStream_t st) {
   const int n = a.nMt * S;
+  const double flops = 2.0 * a.M * a.D * (double)(min(a.V, t1 * TILE) - t0 * TILE);
   const int nl = (n + 7) / 8 * 8;
 #define CCE_FWD2(VEC, KT, CAP, BM)                                                              \
-  hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL, CAP, BM>), dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M,  \
-                     a.V, a.D, a.nMt, S, T, t0, t1, slot0, nl, a.softcap, a.part_m, a.part_s,     \
-                     a.Mpad, a.bm)
+  CCE_TIMED(KN_FWD, flops, st,                                                                  \
+            hipLaunchKernelGGL((k_fwd<VEC, KT, TAIL, CAP, BM>), dim3(nl), dim3(NT), 0, st, a.H,  \
+                               a.W, a.M, a.V, a.D, a.nMt, S, T, t0, t1, slot0, nl, a.softcap,    \
+                               a.part_m, a.part_s, a.Mpad, a.bm))
 #define CCE_FWD(VEC, KT, CAP)                                                                   \
   do {                                                                                          \
     if (a.bm) CCE_FWD2(VEC, KT, CAP, true); else CCE_FWD2(VEC, KT, CAP, false);                \
@@ -460,11 +462,13 @@ hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {
     fwd_split_tiles(a.nMt, nVt, S, T);
     const int nl = (a.nMt * S + 7) / 8 * 8;
     if (a.softcap > 0.f)
-      hipLaunchKernelGGL(k_fwd_tall<true>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D,
-                         a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad);
+      CCE_TIMED(KN_FWD_TALL, 2.0 * a.M * a.V * a.D, st,
+                hipLaunchKernelGGL(k_fwd_tall<true>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V,
+                                   a.D, a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad));
     else
-      hipLaunchKernelGGL(k_fwd_tall<false>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V, a.D,
-                         a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad);
+      CCE_TIMED(KN_FWD_TALL, 2.0 * a.M * a.V * a.D, st,
+                hipLaunchKernelGGL(k_fwd_tall<false>, dim3(nl), dim3(NT), 0, st, a.H, a.W, a.M, a.V,
+                                   a.D, a.nMt, S, T, nVt, nl, a.softcap, a.part_m, a.part_s, a.Mpad));
     slots = S;
     return hipGetLastError();
   }
@@ -483,8 +487,9 @@ hipError_t launch_forward_tiles(const FwdArgs& a, int& slots, hipStream_t st) {
 
 hipError_t launch_forward_merge(const FwdArgs& a, const float* pm, const float* ps, int slots,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, pm, ps, a.tgt, a.y,
-                     a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status);
+  CCE_TIMED(KN_FWD_MERGE, 0.0, st,
+            hipLaunchKernelGGL(k_fwd_merge, dim3((a.M + 255) / 256), dim3(256), 0, st, pm, ps,
+                               a.tgt, a.y, a.M, a.V, slots, a.Mpad, a.logp, a.lse, a.status));
   return hipGetLastError();
 }
 
@@ -492,8 +497,9 @@ hipError_t launch_forward(const FwdArgs& a, hipStream_t st) {
   int slots = 0;
   hipError_t e = launch_forward_tiles(a, slots, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_target_logit, dim3((a.M + 3) / 4), dim3(256), 0, st, a.H, a.W, a.y, a.M, a.V,
-                     a.D, a.softcap, a.tgt);
+  CCE_TIMED(KN_TARGET_LOGIT, 2.0 * a.M * a.D, st,
+            hipLaunchKernelGGL(k_target_logit, dim3((a.M + 3) / 4), dim3(256), 0, st, a.H, a.W,
+                               a.y, a.M, a.V, a.D, a.softcap, a.tgt));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_forward_merge(a, a.part_m, a.part_s, slots, st);
 }

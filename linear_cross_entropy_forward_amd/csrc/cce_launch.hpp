@@ -8,6 +8,28 @@ namespace cce {
 
 typedef unsigned short u16;
 
+// Per-launch timing (the profiling hook cce_timing_begin / cce_timing_end of
+// the C-ABI): every kernel launch is bracketed by timing_pre / timing_post on
+// its stream, which record the caller's events when a timing window is open on
+// the calling thread and do nothing otherwise.  Kinds name the kernels.
+enum LaunchKind : int {
+  KN_FWD = 1, KN_FWD_TALL, KN_TARGET_LOGIT, KN_FWD_MERGE,
+  KN_EPI_BLOCKS, KN_EPI_PAIRS, KN_EPI_FINAL, KN_EPI_COEF, KN_EPI_INIT,
+  KN_RECOMPUTE, KN_RECOMPUTE_TALL, KN_BWD_FUSED, KN_GRADS, KN_SPLIT_REDUCE,
+  KN_DEQUANT, KN_TARGET_LOGIT_Q, KN_FWD_FOLD, KN_TARGET_DH, KN_SORT, KN_TARGET_DW,
+  KN_COUNT
+};
+// FLOPS: the launch's algorithmic floating-point operations (2 per multiply-add
+// of its contractions; 0 for kernels without one).
+void timing_pre(hipStream_t st);
+void timing_post(int kind, double flops, hipStream_t st);
+#define CCE_TIMED(KIND, FLOPS, ST, ...)       \
+  do {                                        \
+    ::cce::timing_pre(ST);                    \
+    __VA_ARGS__;                              \
+    ::cce::timing_post(KIND, (FLOPS), ST);    \
+  } while (0)
+
 // Tile size shared by every kernel (rows of each GEMM operand per workgroup).
 constexpr int kTile = 256;
 // Vocabulary entries per backward chunk: the chunk's bf16 gradient tile
@@ -15,6 +37,9 @@ constexpr int kTile = 256;
 constexpr int kVocabChunk = 16384;
 // Doubles per pair in the epilogue's pair table.
 constexpr int kPairStride = 16;
+// Rows per block of the epilogue's row pass, and the bytes of one run record.
+constexpr int kEpiRows = 2048;
+constexpr int kEpiRecBytes = 48;
 // Compute units of the target chip (MI355X): the workgroups one launch round holds.
 constexpr int kCUs = 256;
 
@@ -84,6 +109,10 @@ struct EpiArgs {
   double beta, gamma;   // s = beta (lw - lr) - gamma (objectives other than ORPO)
   int scope;
   double* pairs;  // [n_pairs, kPairStride]
+  void* rec;      // run records of the row pass: kEpiRows per block of rows
+  int* nruns;     // [blocks]
+  int* first;     // [n_pairs]: first and last block holding each pair
+  int* last;
   float* out5;
   float* pair_stats;  // may be null
   float* coef;
@@ -118,8 +147,21 @@ struct BwdArgs {
   // split-K partials of the dh contraction: room for P_tiles fp32 256 x 256 tiles
   float* P;
   long long P_tiles;
+  // the onehot part of the gradient (taken exactly, outside the bf16 tiles):
+  // t_i per row, and the (target, row) sort's two buffer pairs and histogram
+  float* tc;
+  int* skey[2];
+  int* sval[2];
+  int* shist;
+  float* tF;  // [ceil(M / 64), D]: per window of the sorted rows, a run's first / last piece
+  float* tL;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
+// dh = -t_i W_{y_i} for every row (before the chunks accumulate into it), and
+// t / the sort input; then, after the chunks wrote dW, dW_v -= sum t_i h_i over
+// each target's rows in row order (bf16 head only).
+hipError_t launch_target_dh(const BwdArgs& a, hipStream_t st);
+hipError_t launch_target_dw(const BwdArgs& a, hipStream_t st);
 // Split of one chunk's dh contraction: the tiles from raster index n_full on are
 // computed in ks K-parts (ks = 1: no split); (ks - 1) * (tiles - n_full) partial
 // tiles, at most max_tiles.

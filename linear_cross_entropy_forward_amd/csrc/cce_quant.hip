@@ -61,8 +61,9 @@ __global__ __launch_bounds__(256) void k_dequant(const unsigned* __restrict__ Wq
 
 hipError_t launch_dequant(const QuantW& q, int v0, int vlen, int D, u16* dst, hipStream_t st) {
   const long long n = (long long)vlen * (D * q.bits / 32);
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q.Wq, q.scale,
-                     q.bias, q.bits, q.group, v0, vlen, D, dst);
+  CCE_TIMED(KN_DEQUANT, 0.0, st,
+            hipLaunchKernelGGL(k_dequant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, q.Wq,
+                               q.scale, q.bias, q.bits, q.group, v0, vlen, D, dst));
   return hipGetLastError();
 }
 
@@ -131,12 +132,15 @@ hipError_t launch_forward_quant(const FwdQArgs& a, hipStream_t st) {
     if (vlen / kTile > 0) fwd_split_tiles(c.nMt, vlen / kTile, c.S, c.T);
     int slots = 0;
     if ((e = launch_forward_tiles(c, slots, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_fwd_fold, dim3((f.M + 255) / 256), dim3(256), 0, st, f.part_m, f.part_s,
-                       slots, f.M, f.Mpad, v0 == 0 ? 1 : 0, a.run_m, a.run_s);
+    CCE_TIMED(KN_FWD_FOLD, 0.0, st,
+              hipLaunchKernelGGL(k_fwd_fold, dim3((f.M + 255) / 256), dim3(256), 0, st, f.part_m,
+                                 f.part_s, slots, f.M, f.Mpad, v0 == 0 ? 1 : 0, a.run_m, a.run_s));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_target_logit_q, dim3((f.M + 3) / 4), dim3(256), 0, st, f.H, a.q.Wq,
-                     a.q.scale, a.q.bias, a.q.bits, a.q.group, f.y, f.M, f.V, f.D, f.softcap, f.tgt);
+  CCE_TIMED(KN_TARGET_LOGIT_Q, 2.0 * f.M * f.D, st,
+            hipLaunchKernelGGL(k_target_logit_q, dim3((f.M + 3) / 4), dim3(256), 0, st, f.H,
+                               a.q.Wq, a.q.scale, a.q.bias, a.q.bits, a.q.group, f.y, f.M, f.V,
+                               f.D, f.softcap, f.tgt));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_forward_merge(f, a.run_m, a.run_s, 1, st);
 }

@@ -29,7 +29,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == {"cce_abi_version", "cce_status_string", "cce_workspace_bytes", "cce_forward",
                      "orpo_epilogue", "pref_epilogue", "cce_backward", "cce_workspace_bytes_q",
-                     "cce_forward_q", "cce_backward_q"}
+                     "cce_forward_q", "cce_backward_q", "cce_timing_begin", "cce_timing_end",
+                     "cce_kernel_name"}
     assert names == set(B.SIGNATURES)
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert B.load().cce_abi_version() == 5
+    assert B.load().cce_abi_version() == 6
 
 
 def test_status_strings():
@@ -76,12 +77,13 @@ def test_workspace_small_M_bounded():
 
 
 def test_workspace_bound_at_gemma_and_stress():
-    # the two bf16 gradient chunks dominate: 2 * (2 * Mpad * 16384) bytes, plus < 2 MB per
-    # 8192 rows
-    gemma = B.workspace_bytes(8192, 262144, 2560)
-    stress = B.workspace_bytes(16384, 262144, 4096)
-    assert 4 * 8192 * 16384 <= gemma < 4 * 8192 * 16384 + 2e6
-    assert 4 * 16384 * 16384 <= stress < 4 * 16384 * 16384 + 4e6
+    # the two bf16 gradient chunks dominate: 2 * (2 * Mpad * 16384) bytes; besides them about
+    # 300 bytes a row (forward partials, the epilogue's pair table and run records, the onehot
+    # part's per-row t and sort buffers) and D / 8 bytes a row (the onehot dW pass's window
+    # partials, two fp32 rows of D per 64 sorted rows)
+    for M, D in ((8192, 2560), (16384, 4096)):
+        ws = B.workspace_bytes(M, 262144, D)
+        assert 4 * M * 16384 <= ws < 4 * M * 16384 + 300 * M + M * D // 8 + 1_000_000
 
 
 FAKE = 1 << 20   # a non-null pointer value; never dereferenced on these paths
@@ -234,3 +236,23 @@ def test_valid_call_without_gfx950_is_refused():
     st = lib.cce_forward_q(FAKE, FAKE, FAKE, FAKE, 4, 32, FAKE, 300, 1000, 64, 0.0, FAKE, FAKE, None,
                            FAKE, FAKE * 256, wq, None)
     assert st == B.CCE_EDEVICE
+
+
+def test_timing_hook_host_side():
+    """The timing window's argument checks, names of the kernel kinds, and
+    end-without-begin (no GPU call is made)."""
+    lib = B.load()
+    assert lib.cce_timing_end() == -1
+    kinds = (ctypes.c_int32 * 2)()
+    ev = (ctypes.c_void_p * 4)(1, 2, 3, 0)
+    assert lib.cce_timing_begin(None, kinds, None, 2) == B.CCE_EINVAL
+    assert lib.cce_timing_begin(ev, None, None, 2) == B.CCE_EINVAL
+    assert lib.cce_timing_begin(ev, kinds, None, 0) == B.CCE_EINVAL
+    assert lib.cce_timing_begin(ev, kinds, None, 2) == B.CCE_EINVAL   # a NULL event
+    assert lib.cce_timing_end() == -1
+    names = {lib.cce_kernel_name(k).decode() for k in range(1, 21)}
+    assert {"k_fwd", "k_bwd_fused", "k_grads", "k_recompute_tall", "k_epi_blocks", "k_target_dh",
+            "k_sort", "k_target_dw"} <= names
+    assert "unknown" not in names
+    assert lib.cce_kernel_name(0).decode() == "unknown"
+
