@@ -240,6 +240,25 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
                           uint32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * cce_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that forbid
+ * allocation).  The forward's scratch (the per-split partial max / sum-exp of
+ * each row and the target logits) lives in a fixed 16 MiB array of the
+ * library's own device memory, one per device the library runs on, held until
+ * the process ends; nothing is allocated by the call.  Arguments, outputs and
+ * results are those of cce_forward (the same kernels; bytes identical to it).
+ *   M        at most 786432 rows, else CCE_ESHAPE (the scratch would not fit).
+ * Every call on one device shares that device's array: calls that overlap on
+ * one GPU (on different streams, or from several threads) race and must not
+ * be issued; calls ordered on one stream are fine.  No scratch contents carry
+ * from one call to the next (each call writes before it reads).
+ */
+cce_status cce_forward_noalloc(const void* h, const void* W, const int32_t* y,
+                               int64_t M, int64_t V, int64_t D, float softcap,
+                               float* logp, float* lse, float* block_max, uint32_t* dev_status,
+                               void* stream);
+
+/*
  * Per-launch timing (a profiling hook; no result depends on it).  Between
  * cce_timing_begin and cce_timing_end, every kernel that a call of this
  * library enqueues from the calling thread is bracketed by two of the caller's

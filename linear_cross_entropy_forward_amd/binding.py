@@ -41,6 +41,8 @@ SIGNATURES = {
                              _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]),
     "cce_backward_q": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_p, _c_p, _c_p, _c_p, _c_i64,
                               _c_i64, _c_i64, _c_f, _c_f, _c_f, _c_p, _c_p, _c_p, _c_sz, _c_p]),
+    "cce_forward_noalloc": (_c_i, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_f, _c_p, _c_p, _c_p,
+                                   _c_p, _c_p]),
     "cce_timing_begin": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_int32]),
     "cce_timing_end": (ctypes.c_int32, []),
     "cce_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -287,6 +289,30 @@ class Head:
 
     def clear_status(self):
         self.status.zero_()
+
+
+NOALLOC_MAX_M = 786432
+
+
+def forward_noalloc(h, W, y, status, logp=None, lse=None, stream=None, softcap: float = 0.0,
+                    block_max=None):
+    """cce_forward through its no-allocation variant (scratch in the library's
+    fixed device array; M <= NOALLOC_MAX_M).  status: an int32 [1] device tensor
+    (the device status word)."""
+    M, D = int(h.shape[0]), int(h.shape[1])
+    V = int(W.shape[0])
+    if logp is None:
+        logp = torch.empty(M, dtype=torch.float32, device=h.device)
+    if lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=h.device)
+    st = load().cce_forward_noalloc(_bf16(h, "h", (M, D)), _bf16(W, "W", (V, D)),
+                                    _dev(y, "y", torch.int32, (M,)), M, V, D, float(softcap),
+                                    _dev(logp, "logp", torch.float32, (M,)),
+                                    _dev(lse, "lse", torch.float32, (M,)),
+                                    _opt(block_max, "block_max", block_max_shape(M, V)),
+                                    _dev(status, "status", torch.int32, (1,)), _stream_ptr(stream))
+    _check("cce_forward_noalloc", st)
+    return logp, lse
 
 
 class LaunchTimer:

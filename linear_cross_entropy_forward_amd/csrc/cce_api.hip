@@ -147,6 +147,53 @@ void set_target_regions(cce::BwdArgs& a, const Layout& L, char* base) {
   a.tL = reinterpret_cast<float*>(base + L.tL);
 }
 
+// Scratch of the no-allocation forward (cce_forward_noalloc): one array per
+// device, held for the life of the process.  Host code never uses its name as
+// an address: each device's copy is found with hipGetSymbolAddress (once per
+// device, with that device current) and only that pointer is passed on.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int64_t kNoAllocMaxM = 786432;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Forward-only layout: partial (max, sum-exp) slots and the target logits.
+struct FwdLayout {
+  int64_t Mpad, nMt;
+  size_t part_m, part_s, tgt, total;
+};
+FwdLayout fwd_layout(int64_t M) {
+  FwdLayout L{};
+  L.nMt = (M + kTile - 1) / kTile;
+  L.Mpad = L.nMt * kTile;
+  const int64_t Scap = fwd_split_cap(L.nMt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.part_m = take((size_t)Scap * L.Mpad * sizeof(float));
+  L.part_s = take((size_t)Scap * L.Mpad * sizeof(float));
+  L.tgt = take((size_t)L.Mpad * sizeof(float));
+  L.total = off;
+  return L;
+}
+static_assert(kNoAllocMaxM <= kMaxM, "no-allocation row limit within the library's");
+
+// This device's scratch address (cached per device id); null on failure.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 // The calling thread's timing window (cce_timing_begin .. cce_timing_end).
 struct TimingLog {
   void* const* ev;  // 2 * cap caller-owned events: before / after launch i
@@ -264,6 +311,43 @@ cce_status cce_forward(const void* h, const void* W, const int32_t* y, int64_t M
   a.nVt = (int)((V + kTile - 1) / kTile);
   a.S = a.T = 0;
   if (V / kTile > 0) cce::fwd_split_tiles(a.nMt, (int)(V / kTile), a.S, a.T);  // full vocab tiles
+  a.Mpad = (int)L.Mpad;
+  a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
+  a.softcap = softcap;
+  a.part_m = reinterpret_cast<float*>(base + L.part_m);
+  a.part_s = reinterpret_cast<float*>(base + L.part_s);
+  a.tgt = reinterpret_cast<float*>(base + L.tgt);
+  a.logp = logp;
+  a.lse = lse;
+  a.status = dev_status;
+  a.bm = block_max;
+  return cce::launch_forward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
+                                                                               : CCE_ELAUNCH;
+}
+
+cce_status cce_forward_noalloc(const void* h, const void* W, const int32_t* y, int64_t M,
+                               int64_t V, int64_t D, float softcap, float* logp, float* lse,
+                               float* block_max, uint32_t* dev_status, void* stream) {
+  if (!h || !W || !y || !logp || !lse || !dev_status) return CCE_EINVAL;
+  if (!(softcap >= 0.f) || !isfinite(softcap)) return CCE_EINVAL;
+  if (!sizes_ok(M, V, D) || M > kNoAllocMaxM) return CCE_ESHAPE;
+  const FwdLayout L = fwd_layout(M);
+  if (L.total > kScratchBytes) return CCE_ESHAPE;
+  const cce_status ds = device_ok();
+  if (ds != CCE_OK) return ds;
+  char* base = static_cast<char*>(scratch_ptr());
+  if (!base) return CCE_EDEVICE;
+  cce::FwdArgs a{};
+  a.H = static_cast<const cce::u16*>(h);
+  a.W = static_cast<const cce::u16*>(W);
+  a.y = y;
+  a.M = (int)M;
+  a.V = (int)V;
+  a.D = (int)D;
+  a.nMt = (int)L.nMt;
+  a.nVt = (int)((V + kTile - 1) / kTile);
+  a.S = a.T = 0;
+  if (V / kTile > 0) cce::fwd_split_tiles(a.nMt, (int)(V / kTile), a.S, a.T);
   a.Mpad = (int)L.Mpad;
   a.vec = (D % 8 == 0) && aligned16(h) && aligned16(W);
   a.softcap = softcap;

@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
     assert names == {"cce_abi_version", "cce_status_string", "cce_workspace_bytes", "cce_forward",
                      "orpo_epilogue", "pref_epilogue", "cce_backward", "cce_workspace_bytes_q",
                      "cce_forward_q", "cce_backward_q", "cce_timing_begin", "cce_timing_end",
-                     "cce_kernel_name"}
+                     "cce_kernel_name", "cce_forward_noalloc"}
     assert names == set(B.SIGNATURES)
 
 
@@ -256,3 +256,32 @@ def test_timing_hook_host_side():
     assert "unknown" not in names
     assert lib.cce_kernel_name(0).decode() == "unknown"
 
+
+def test_forward_noalloc_argument_errors():
+    """Host checks of the no-allocation forward, before any HIP call: NULLs, a bad
+    cap, bad sizes, and M above the fixed scratch's limit."""
+    lib = B.load()
+    f = lib.cce_forward_noalloc
+    args = [FAKE, FAKE, FAKE, 100, 200, 64, 0.0, FAKE, FAKE, None, FAKE, None]
+    for i in (0, 1, 2, 7, 8, 10):
+        a = list(args)
+        a[i] = None
+        assert f(*a) == B.CCE_EINVAL, i
+    a = list(args)
+    a[6] = -1.0
+    assert f(*a) == B.CCE_EINVAL
+    for M, V, D in ((0, 10, 10), (10, 0, 10), (10, 10, 0), (B.NOALLOC_MAX_M + 1, 10, 10)):
+        a = list(args)
+        a[3:6] = [M, V, D]
+        assert f(*a) == B.CCE_ESHAPE, (M, V, D)
+    # within the limit the call gets past the size checks and, with no GPU visible,
+    # stops at the device check (never reached with a GPU: the pointers are fake)
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return
+    except Exception:
+        pass
+    a = list(args)
+    a[3] = B.NOALLOC_MAX_M
+    assert f(*a) == B.CCE_EDEVICE
