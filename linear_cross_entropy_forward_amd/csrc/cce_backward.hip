@@ -413,6 +413,43 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int lane) {
   v[3] = even ? t[2] : v[3];
 }
 
+// Output tiles leave the accumulators through LDS, one 32-row band of a
+// wave's 128 columns at a time, so that each global load or store instruction
+// covers two runs of 512 contiguous bytes (lane l: row 2k + l / 32, columns
+// 4 (l % 32) ..): the per-CU store path moves about 3x more bytes per second
+// that way than with the quad-transposed layout's 8 rows x 128 bytes per
+// instruction.  Each wave owns kBandBytes of LDS at w * kBandBytes (the
+// operand ring is free once the K loop has returned); the row pitch 576 bytes
+// puts rows r and r + 1 16 banks apart, so neither the 16-byte writes of the
+// quad-transposed fragments nor the row reads conflict within 16 lanes.  LDS
+// accesses of one wave complete in order, so a band's reads see its writes
+// and the next band's writes wait for them.
+constexpr int kBandPitch = 576;
+constexpr int kBandBytes = 32 * kBandPitch;
+
+// Band rows 0..31 x columns 0..127 from t[jj] (32 x 32 accumulator tiles).
+__device__ __forceinline__ void band_put(unsigned char* band, const floatx16 (&t)[4], int lane) {
+  const int half = lane >> 5;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float v[4] = {t[jj][4 * r4], t[jj][4 * r4 + 1], t[jj][4 * r4 + 2], t[jj][4 * r4 + 3]};
+      quad_transpose(v, lane);
+      const int row = 8 * r4 + 4 * half + (lane & 3);
+      const int col = jj * 32 + (lane & 28);
+      *reinterpret_cast<float4*>(band + row * kBandPitch + col * 4) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Rows 2k and 2k + 1 of a band: lane l gets columns 4 (l % 32) .. + 3 of row
+// 2k + l / 32.
+__device__ __forceinline__ float4 band_get(const unsigned char* band, int k, int lane) {
+  return *reinterpret_cast<const float4*>(band + (2 * k + (lane >> 5)) * kBandPitch +
+                                          (lane & 31) * 16);
+}
+
 // The dh and dW contractions of one vocab chunk in a single launch: workgroups
 // [0, p0.nl) take p0 (dh, the longer K), the rest take p1 (dW).  Dispatching
 // the long tiles first lets the short ones fill the tail, so the two problems
@@ -431,6 +468,25 @@ __device__ __forceinline__ void dw_tall_task(const GemmProb& p, int ta, int tb, 
   AccTall acc;
   gemm_tile_tall<true>(at, bo, p.K, sm, acc);
   const bool vec4 = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
+  if (vec4 && (ta + 1) * TALL <= p.c_rows && (tb + 1) * TILE <= p.c_cols) {
+    // the whole tile inside C: row-contiguous stores through this wave's band
+    unsigned char* const band = sm.raw + w * kBandBytes;
+    float* const c0 = p.C + (size_t)(ta * TALL + wi * 192) * p.ldc + tb * TILE + wj * 128 +
+                      (lane & 31) * 4;
+    auto flush = [&](const floatx16 (&t)[4], int ii) {
+      band_put(band, t, lane);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        *reinterpret_cast<float4*>(c0 + (size_t)(ii * 32 + 2 * k + half) * p.ldc) =
+            band_get(band, k, lane);
+    };
+    // the VGPR part first, so its registers are free before the AGPRs are read
+    flush(acc.v[0], 4);
+    flush(acc.v[1], 5);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) flush(acc.a[ii], ii);
+    return;
+  }
   auto put = [&](const floatx16& t, int ii, int jj) {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -514,6 +570,44 @@ __device__ __forceinline__ void grads_task(const GemmProb& p0, const GemmProb& p
   // accumulated) as 16 bytes when C's rows are 16-byte aligned.
   float* const Cb = p.C;
   const bool vec4 = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15u) == 0;
+  if (!SKIP && vec4 && (ta + 1) * TILE <= p.c_rows && (tb + 1) * TILE <= p.c_cols) {
+    // The whole tile inside C: row-contiguous loads and stores through this
+    // wave's band.  The accumulation reads two bands of C (2 x 16 x 16 bytes a
+    // lane) before it adds and stores them: a store may alias a later read, so
+    // reading each piece just before its store would cost one memory round
+    // trip per piece.
+    unsigned char* const band = sm.raw + w * kBandBytes;
+    float* const c0 = Cb + (size_t)(ta * TILE + wi * 128) * p.ldc + tb * TILE + wj * 128 +
+                      (lane & 31) * 4;
+#pragma unroll
+    for (int i2 = 0; i2 < 4; i2 += 2) {
+      float4 q[2][16];
+      if (accum) {
+#pragma unroll
+        for (int di = 0; di < 2; ++di)
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            q[di][k] = *reinterpret_cast<const float4*>(
+                c0 + (size_t)((i2 + di) * 32 + 2 * k + half) * p.ldc);
+      }
+#pragma unroll
+      for (int di = 0; di < 2; ++di) {
+        band_put(band, acc[i2 + di], lane);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          float4 o = band_get(band, k, lane);
+          if (accum) {
+            o.x += q[di][k].x;
+            o.y += q[di][k].y;
+            o.z += q[di][k].z;
+            o.w += q[di][k].w;
+          }
+          *reinterpret_cast<float4*>(c0 + (size_t)((i2 + di) * 32 + 2 * k + half) * p.ldc) = o;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
