@@ -48,6 +48,15 @@ struct __align__(16) Smem {
 // ---------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------
+// The work-item index, opaque to the optimiser: values derived from it are
+// computed where they are used rather than hoisted to the top of the kernel,
+// where they would stay live through the K loops and be spilled.
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Two fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
@@ -660,7 +669,7 @@ __device__ __forceinline__ void gemm_tile(const OpRef& A, const OpRef& B, int K,
                                           const int* __restrict__ kflags, int kflag_stride,
                                           Smem& sm, floatx16 (&acc)[4][4]) {
   constexpr bool AK = AMODE >= OP_KROW, BKM = BMODE >= OP_KROW;
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int wi = w & 1, wj = w >> 1;
@@ -946,7 +955,7 @@ __device__ __forceinline__ void tall_step(const typename TallForms<KF>::DA& da,
 template <bool KF>
 __device__ __forceinline__ void gemm_tile_tall(const OpRef& A, const OpRef& B, int K, SmemTall& sm,
                                                AccTall& acc) {
-  const int tid = threadIdx.x;
+  const int tid = opaque_tid();
   const int lane = tid & 63;
   const int w = tid >> 6;
   tall_zero(acc);
@@ -1081,7 +1090,7 @@ __device__ __forceinline__ void sub64(const Dma128& da, const Dma128& db, const 
 // at `ring`.  Ends with every load drained and a barrier (LDS free).
 __device__ __forceinline__ void gemm_tile64(const OpRef& A, const OpRef& B, int K, unsigned char* ring,
                                             floatx16 (&acc)[4][4]) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = opaque_tid(), lane = tid & 63, w = tid >> 6;
   zero_acc(acc);
   Frag64 fa;
   fa.init(lane, w & 1, w >> 1);
