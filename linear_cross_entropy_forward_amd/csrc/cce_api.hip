@@ -47,6 +47,7 @@ struct Layout {
   // quantised head only: running (max, sum-exp), the bf16 chunk buffer and its
   // own dh partials (no dW there, so dh splits further)
   size_t run_m, run_s, wbuf, psplit_q;
+  size_t g2q, wbuf2;  // the pipelined quantised backward's second G and chunk buffers (0: none)
   long long psplit_tiles_q;
   size_t total_q;
 };
@@ -108,6 +109,10 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.run_m = take((size_t)L.Mpad * sizeof(float));
   L.run_s = take((size_t)L.Mpad * sizeof(float));
   L.wbuf = take((size_t)L.Vc * D * 2);
+  // the pipelined quantised backward (tall tiles, D % 32 == 0) alternates
+  // between two gradient buffers and two dequantised chunk buffers
+  L.g2q = D % 32 == 0 ? take((size_t)L.Mpad * L.Vc * 2) : 0;
+  L.wbuf2 = D % 32 == 0 ? take((size_t)L.Vc * D * 2) : 0;
   L.psplit_tiles_q = split_tiles(L, false);
   L.psplit_q = take((size_t)L.psplit_tiles_q * kTile * kTile * 4);
   L.total_q = off;
@@ -567,6 +572,8 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
   a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);
+  a.G2 = L.g2q ? reinterpret_cast<cce::u16*>(base + L.g2q) : nullptr;
+  a.Wbuf2 = L.wbuf2 ? reinterpret_cast<cce::u16*>(base + L.wbuf2) : nullptr;
   return cce::launch_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? CCE_OK
                                                                                 : CCE_ELAUNCH;
 }

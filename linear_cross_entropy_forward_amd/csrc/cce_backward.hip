@@ -771,14 +771,14 @@ static int tall_chunk(int Vc, int nMt) {
 // The dh / dW problems of one vocab chunk [v0, v0 + vlen) over the gradient
 // buffer G (see the kernels above for the operand forms).
 static void grads_probs(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* G, GemmProb& dh,
-                        GemmProb& dw, DhSplit& sp, bool tall_dw = false) {
+                        GemmProb& dw, DhSplit& sp, bool tall_dw = false, bool no_split = false) {
   const int nDt = a.Dpad / kTile;
   const int nkbV = a.Vc / 32;
   const int nvt = (vlen + kTile - 1) / kTile;
   const int fstride = a.Vc / kTile;
   const bool with_dw = a.q.Wq == nullptr;
-  sp = dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.P_tiles);
   const int nT = a.nMt * nDt;
+  sp = no_split ? DhSplit{1, nT} : dh_split(a.nMt, nDt, nvt, with_dw, a.Mpad, a.P_tiles);
   const int dh_nl =
       sp.ks == 1 ? pad8(nT) : 8 * (sp.n_full / 8 + ((nT - sp.n_full) * sp.ks + 7) / 8);
   // dh accumulates into what launch_target_dh wrote (the onehot part)
@@ -881,6 +881,56 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
     }
     return launch_target_dw(a, st);
+  }
+
+  // Pipelined quantised form (tall recompute, second gradient and chunk
+  // buffers): chunk c + 1 is dequantised into the other chunk buffer before
+  // launch c, which runs chunk c's dh tasks (no dW: the quantised head is
+  // frozen) and chunk c + 1's recompute tiles.  The chunk buffer it overwrites
+  // was last read by the dh tasks of launch c - 1, which has finished; the
+  // gradient buffers alternate as above.  The dh tiles are not split over K
+  // here: the recompute tiles fill the launch's rounds.
+  if (tall && a.q.Wq != nullptr && a.G2 != nullptr && a.Wbuf2 != nullptr) {
+    u16* const Gb[2] = {a.G, a.G2};
+    u16* const Wb[2] = {a.Wbuf, a.Wbuf2};
+    if ((e = launch_dequant(a.q, 0, chunks[0].second, a.D, Wb[0], st)) != hipSuccess) return e;
+    {
+      const RecArgs r = rec_args(a, 0, chunks[0].second, Wb[0], Gb[0]);
+#define CCE_REC(FILT, CAP)                                                                    \
+  CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
+      if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
+      else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
+#undef CCE_REC
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    for (int c = 0; c < nch; ++c) {
+      const int v0 = chunks[c].first, vlen = chunks[c].second;
+      const bool last = c + 1 == nch;
+      GemmProb dh, dw;
+      DhSplit sp;
+      grads_probs(a, v0, vlen, Wb[c & 1], Gb[c & 1], dh, dw, sp, false, !last);
+      if (!last) {
+        const int v1 = chunks[c + 1].first, vlen1 = chunks[c + 1].second;
+        if ((e = launch_dequant(a.q, v1, vlen1, a.D, Wb[(c + 1) & 1], st)) != hipSuccess) return e;
+        const RecArgs r = rec_args(a, v1, vlen1, Wb[(c + 1) & 1], Gb[(c + 1) & 1]);
+        dw.nl = 0;  // dh tasks only
+        const dim3 grid(dh.nl + r.nl);
+#define CCE_FUSED(FILT, CAP)                                                                  \
+  CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * ((double)vlen + r.vlen), st,                      \
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r))
+        if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
+        else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
+#undef CCE_FUSED
+      } else {
+        CCE_TIMED(KN_GRADS, 2.0 * a.M * a.D * vlen, st,
+                  hipLaunchKernelGGL((k_grads<false, true>), dim3(dh.nl), dim3(NT), 0, st, dh,
+                                     dw));
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 
   for (int c = 0; c < nch; ++c) {

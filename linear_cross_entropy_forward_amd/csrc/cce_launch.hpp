@@ -141,6 +141,7 @@ struct BwdArgs {
   // and dW is not formed (the quantised head is frozen; dW may be null)
   QuantW q;
   u16* Wbuf;
+  u16* Wbuf2;  // null, or a second chunk buffer (the pipelined quantised backward)
   // null, or the forward's saved block maximum ([ceil(V / 256), M]): with
   // block_eps > 0 a tile's skip is decided from it before its recompute
   const float* bm;

@@ -167,19 +167,20 @@ def test_backward_argument_errors():
     assert lib.cce_backward(*a) == B.CCE_EWORKSPACE
 
 
-def test_quant_workspace_adds_one_chunk_buffer():
+def test_quant_workspace_adds_two_chunk_buffers():
     M, D = 8192, 2560
     sizes = [B.workspace_bytes_q(M, V, D) for V in (32768, 262144, 1 << 20)]
     assert len(set(sizes)) == 1
-    # the bf16 head's workspace less its second gradient buffer (the quantised
-    # head's backward is not pipelined)
-    bf16 = B.workspace_bytes(M, 262144, D) - 2 * M * 16384
+    # both backwards are pipelined over two gradient buffers; the quantised one
+    # adds two bf16 chunk buffers of the dequantised head (16384 x D each), two
+    # fp32 rows of Mpad, and its own split dh partials (at most 7 fp32 M x D
+    # buffers) in place of the bf16 head's
+    bf16 = B.workspace_bytes(M, 262144, D)
     extra = sizes[0] - bf16
-    # the bf16 chunk of the dequantised head (16384 x D), two fp32 rows of Mpad, and
-    # at most 7 fp32 M x D partial buffers of the split dh contraction
-    assert 2 * 16384 * D + 8 * M <= extra <= 2 * 16384 * D + 8 * M + 7 * M * D * 4 + 4 * 256
+    assert 2 * 2 * 16384 * D + 8 * M - 7 * M * D * 4 <= extra
+    assert extra <= 2 * 2 * 16384 * D + 8 * M + 7 * M * D * 4 + 4 * 256
     # the partials stay within half the gradient chunk
-    assert sizes[0] <= bf16 + 2 * 16384 * D + 8 * M + 8192 * 16384 + 4 * 256
+    assert sizes[0] <= bf16 + 2 * 2 * 16384 * D + 8 * M + 8192 * 16384 + 4 * 256
     assert B.workspace_bytes_q(0, 10, 64) == 0
 
 
