@@ -249,6 +249,23 @@ def filter_deviation(head, h, W, y, lse, coef, feps, dh, dW, bwd_ms, softcap, bm
     return dev
 
 
+def head_bytes_per_step(V, D, bits, group):
+    """Algorithmic bytes of the head moved per step (each pass reads it once).
+    bf16: the forward, the recompute and the dh contraction each read V x D bf16.
+    Quantised: the forward and the backward each dequantise the head once (codes,
+    bf16 scales and biases read; a bf16 chunk buffer written), and the three
+    contractions read the chunk buffers; the frozen head has no dW."""
+    bf16 = V * D * 2
+    if not bits:
+        return {"bf16_head_read": 3 * bf16, "total": 3 * bf16}
+    packed = V * D * bits // 8 + V * (D // group) * 2 * 2
+    out = {"packed_read": 2 * packed, "chunk_buffer_write": 2 * bf16,
+           "chunk_buffer_read": 3 * bf16}
+    out["total"] = sum(out.values())
+    out["bf16_head_equivalent"] = 3 * bf16
+    return out
+
+
 def main():
     args = parse()
     if args.v_sweep:
@@ -446,6 +463,7 @@ def main():
         "phase_ms": {"forward": round(fwd_ms, 4), "epilogue": round(epi_ms, 4),
                      "backward": round(bwd_ms, 4)},
         "workspace_bytes": (B.workspace_bytes_q if quant else B.workspace_bytes)(wl.M, wl.V, wl.D),
+        "head_bytes_per_step": head_bytes_per_step(wl.V, wl.D, args.quant if quant else 0, args.group),
         "device_status": status,
         # the dominant kernel (largest share of the step), timed live per launch with the
         # library's events on the stream it runs on (bench pass 2, the same K steps); FLOPs
