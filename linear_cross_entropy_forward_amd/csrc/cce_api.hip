@@ -37,7 +37,7 @@ int64_t fwd_split_cap(int64_t nMt) { return 256 / nMt + 2; }
 
 struct Layout {
   int64_t Mpad, Dpad, Vc, nMt;
-  size_t part_m, part_s, tgt, pairs, g, flags;
+  size_t part_m, part_s, tgt, pairs, g, flags, flags2;
   size_t epi_rec, epi_nruns, epi_first, epi_last, epi_end;  // the epilogue's row-pass state
   size_t tc, skey[2], sval[2], shist, tF, tL;  // the backward's exact onehot part
   size_t g2;  // the second gradient buffer of the pipelined backward (0: none)
@@ -98,6 +98,7 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.tL = take((size_t)((M + 63) / 64) * D * sizeof(float));
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
+  L.flags2 = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   const size_t base = off;
   // the pipelined backward (tall recompute tiles, D % 32 == 0) alternates
   // between two gradient buffers
@@ -465,6 +466,7 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y, const fl
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
   a.G2 = L.g2 ? reinterpret_cast<cce::u16*>(base + L.g2) : nullptr;
   a.flags = reinterpret_cast<int*>(base + L.flags);
+  a.flags2 = reinterpret_cast<int*>(base + L.flags2);
   a.status = dev_status;
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit);
@@ -564,6 +566,7 @@ cce_status cce_backward_q(const void* h, const uint32_t* Wq, const void* scales,
   a.dW = nullptr;
   a.G = reinterpret_cast<cce::u16*>(base + L.g);
   a.flags = reinterpret_cast<int*>(base + L.flags);
+  a.flags2 = reinterpret_cast<int*>(base + L.flags2);
   a.status = dev_status;
   a.bm = block_max;
   a.P = reinterpret_cast<float*>(base + L.psplit_q);

@@ -257,10 +257,58 @@ struct RecArgs {
   int nkbV;  // 32-wide vocab blocks per token tile of G
   int nkb;   // blocks the dh contraction reads
   int nl;    // workgroups of the recompute (a multiple of 8)
+  // block skip (the SKIP forms): per (token tile, 256-entry vocab block) flags
+  // of this chunk, the chunk's part of the forward's saved block maximum (or
+  // null: the skip is decided from the recomputed entries), and the bound
+  int* flags;
+  const float* bm;
+  float block_eps;
 };
 
-// Recompute task b (of r.nl) of a chunk: one tall tile.
-template <bool FILTER, bool CAP>
+// Whether v holds for any thread of the workgroup, through 16 bytes of LDS at
+// `scratch` (the operand ring, which must not be in use: the tall tile's 160
+// KB leave no room for the reduction __syncthreads_or would add).
+__device__ __forceinline__ bool block_any(bool v, unsigned char* scratch) {
+  const unsigned long long m = __ballot(v);
+  volatile int* const s = reinterpret_cast<volatile int*>(scratch);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = m != 0ull ? 1 : 0;
+  __syncthreads();
+  const bool r = (s[0] | s[1] | s[2] | s[3]) != 0;
+  __syncthreads();
+  return r;
+}
+
+// The skip flag of 256-entry vocab block bb of token tile mt, as tall tile vt
+// (of nvt3) sees it.  A block that lies inside the tile is written whole; one
+// shared with a neighbouring tile is written by halves: 16 bits each, the
+// lower by the tile below, the upper by the tile above, so that each half has
+// one writer and the 32-bit flag the contractions read is nonzero when either
+// part of the block is live.  Every flag of the chunk is written on every
+// pass, so none is left from an earlier chunk.
+__device__ __forceinline__ void put_block_flag(int* flags, int fstride, int mt, int bb, int vt,
+                                               int nvt3, bool live) {
+  int* const f = flags + (size_t)mt * fstride + bb;
+  const int lo = bb * TILE, t0 = vt * TALL;
+  if (lo < t0)
+    reinterpret_cast<unsigned short*>(f)[1] = live ? 1 : 0;
+  else if (lo + TILE > t0 + TALL && vt + 1 < nvt3)
+    reinterpret_cast<unsigned short*>(f)[0] = live ? 1 : 0;
+  else
+    *f = live ? 1 : 0;
+}
+
+// Recompute task b (of r.nl) of a chunk: one tall tile.  SKIP: the block skip
+// of (token tile, 256-entry vocab block) pairs.  A tall tile overlaps two such
+// blocks (the first whole and half of the next, or half of one and the next
+// whole).  With the saved block maximum the test comes first: each block's
+// liveness is decided from it (exp(bm - lse) >= block_eps for some token, or a
+// token's target in the block), and a tile whose blocks are both dead is not
+// recomputed at all.  Without it the tile is recomputed, its largest softmax
+// entry taken per block part, and the parts' votes combine in the block's flag
+// (put_block_flag); the tile's gradient entries are stored either way, and the
+// contractions leave out the dead blocks.
+template <bool FILTER, bool CAP, bool SKIP = false>
 __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, SmemTall& sm) {
   const u16* __restrict__ H = r.H;
   const u16* __restrict__ Wc = r.Wc;
@@ -274,6 +322,29 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
   const int wi = w & 1, wj = w >> 1, half = lane >> 5;
   int mt, vt;
   if (!map_tile(b, r.nl, r.nMt, r.nvt, 8, mt, vt)) return;
+  const int nblk = nkb / 8, fstride = nkbV / 8;
+  const int b_lo = vt * TALL / TILE;
+  const bool two = b_lo + 1 < nblk && vt * TALL + TALL > (b_lo + 1) * TILE;
+  if (SKIP && r.bm) {
+    // one token per thread
+    const int j = mt * TILE + tid;
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q == 1 && !two) break;
+      const int bb = b_lo + q;
+      int keep = 0;
+      if (j < M) {
+        const float pm = fast_exp2((r.bm[(size_t)bb * M + j] - lse[j]) * LOG2E);
+        const int o = y[j] - (v0 + bb * TILE);
+        keep = (pm >= r.block_eps || (unsigned)o < (unsigned)TILE) ? 1 : 0;
+      }
+      const bool live = block_any(keep != 0, sm.raw);
+      if (tid == 0) put_block_flag(r.flags, fstride, mt, bb, vt, r.nvt, live);
+      any |= live;
+    }
+    if (!any) return;
+  }
 
   AccTall acc;
   gemm_tile_tall<false>(OpRef{Wc + (size_t)vt * TALL * D, D, min(TALL, vlen - vt * TALL), D},
@@ -298,6 +369,45 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
   const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
   const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;  // the cap's tanh is taken at the store
   const bool vtail = vt * TALL + TALL > vlen;
+  if (SKIP && !r.bm) {
+    // the largest softmax entry of each block part: tile rows below `split`
+    // are in block b_lo, the rest in b_lo + 1 (split is 256 or 128, a multiple
+    // of the 32-row MFMA tiles)
+    const int split = (b_lo + 1) * TILE - vt * TALL;
+    float pm[2] = {0.f, 0.f};
+    bool tg[2] = {false, false};
+    auto part_max = [&](const floatx16(&t)[4], int row0) {
+      const int q = row0 >= split ? 1 : 0;
+#pragma unroll
+      for (int r16 = 0; r16 < 16; ++r16) {
+        const bool vbad = vt * TALL + row0 + 8 * (r16 >> 2) + 4 * half + (r16 & 3) >= vlen;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float z = CAP ? tanh_scaled(t[jj][r16], k2) : t[jj][r16];
+          const float p = fast_exp2(fmaf(z, c1, nlse[jj]));
+          if (!vbad) pm[q] = fmaxf(pm[q], p);
+        }
+      }
+    };
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) part_max(acc.a[ii], wi * 192 + ii * 32);
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) part_max(acc.v[ii], wi * 192 + 128 + ii * 32);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
+      const int yy = j < M ? y[j] : -1;
+      const int o = yy >= 0 ? yy - (v0 + b_lo * TILE) : -1;
+      tg[0] |= (unsigned)o < (unsigned)TILE;
+      tg[1] |= (unsigned)(o - TILE) < (unsigned)TILE;
+    }
+    const bool live0 = block_any(pm[0] >= r.block_eps || tg[0], sm.raw);
+    const bool live1 = block_any(pm[1] >= r.block_eps || tg[1], sm.raw);
+    if (tid == 0) {
+      put_block_flag(r.flags, fstride, mt, b_lo, vt, r.nvt, live0);
+      if (two) put_block_flag(r.flags, fstride, mt, b_lo + 1, vt, r.nvt, live1);
+    }
+  }
   const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
   const int b0 = vt * 12 + wi * 6;  // this wave's first vocab block of the chunk
   const int nb = min(max(nkb - b0, 0), 6);
@@ -318,10 +428,10 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
 #undef CCE_STORE
 }
 
-template <bool FILTER, bool CAP>
+template <bool FILTER, bool CAP, bool SKIP>
 __global__ __launch_bounds__(NT, 1) void k_recompute_tall(RecArgs r) {
   __shared__ SmemTall sm;
-  recompute_tall_tile<FILTER, CAP>(r, blockIdx.x, sm);
+  recompute_tall_tile<FILTER, CAP, SKIP>(r, blockIdx.x, sm);
 }
 
 // One fp32-output contraction C[ta*256 + i][tb*256 + j] (+)= sum_k A[i][k] B[j][k]
@@ -651,12 +761,14 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 // long dh tasks go first, then dW, then the recompute tiles; the two kinds
 // fill each other's partial rounds, and the recompute's gradient stores
 // overlap other workgroups' contractions.
-template <bool FILTER, bool CAP>
+// SKIP: the block skip (256-row dW tiles and the compacted K loops of the
+// contractions read the flags the previous launch's recompute tiles wrote).
+template <bool FILTER, bool CAP, bool SKIP>
 __global__ __launch_bounds__(NT, 1) void k_bwd_fused(GemmProb p0, GemmProb p1, RecArgs r) {
   __shared__ SmemTall sm;
   const int b = blockIdx.x, ng = p0.nl + p1.nl;
-  if (b < ng) grads_task<false, true>(p0, p1, b, sm);
-  else recompute_tall_tile<FILTER, CAP>(r, b - ng, sm);
+  if (b < ng) grads_task<SKIP, true>(p0, p1, b, sm);
+  else recompute_tall_tile<FILTER, CAP, SKIP>(r, b - ng, sm);
 }
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
@@ -803,7 +915,7 @@ static RecArgs rec_args(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* 
   const int nvt3 = (vlen + TALL - 1) / TALL;
   return RecArgs{a.H,     Wc,           a.y, a.lse, a.coef, a.M, a.D,        v0,
                  vlen,    a.nMt,        nvt3, a.softcap, a.filter_eps, G, a.Vc / 32,
-                 (vlen + kTile - 1) / kTile * 8, pad8(a.nMt * nvt3)};
+                 (vlen + kTile - 1) / kTile * 8, pad8(a.nMt * nvt3), nullptr, nullptr, 0.f};
 }
 
 static hipError_t split_reduce(const GemmProb& dh, const DhSplit& sp, hipStream_t st) {
@@ -821,8 +933,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   const bool filt = a.filter_eps > 0.f;
   const bool cap = a.softcap > 0.f;
   // tall recompute tiles (and the pipelined backward) need aligned row-major
-  // operands with D % 32 == 0, and no tile skip (kept per 256x256 tile)
-  const bool tall = a.vec && a.D % BK == 0 && !(a.block_eps > 0.f);
+  // operands with D % 32 == 0; with a tile skip only the pipelined bf16 form
+  // takes them (its recompute keeps the flags per 256-entry block)
+  const bool skip = a.block_eps > 0.f;
+  const bool tall_ok = a.vec && a.D % BK == 0;
+  const bool pipe = tall_ok && a.q.Wq == nullptr && a.G2 != nullptr && a.flags2 != nullptr;
+  const bool tall = tall_ok && (pipe || !skip);
   const int vstep = tall ? tall_chunk(a.Vc, a.nMt) : a.Vc;
   // the vocabulary chunks; the last one takes whatever is left when it fits
   // the workspace width (no short remainder chunk that runs the chip a
@@ -842,15 +958,31 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
   // every dependence: chunk c's buffer is complete before the launch that
   // reads it, and is rewritten (by chunk c + 2's recompute) only in the launch
   // after the one that read it; dh accumulates chunk by chunk as before.
-  if (tall && a.q.Wq == nullptr && a.G2 != nullptr) {
+  //
+  // With the block skip, each recompute also writes its chunk's flags (one
+  // array per gradient buffer), and the contractions take 256-row dW tiles and
+  // the compacted K loops that leave the dead blocks out.
+  if (pipe) {
     u16* const Gb[2] = {a.G, a.G2};
+    int* const Fl[2] = {a.flags, a.flags2};
+    auto with_skip = [&](RecArgs r, int v, int par) {
+      if (skip) {
+        r.flags = Fl[par];
+        r.bm = a.bm ? a.bm + (size_t)(v / kTile) * a.M : nullptr;
+        r.block_eps = a.block_eps;
+      }
+      return r;
+    };
     {
-      const RecArgs r = rec_args(a, 0, chunks[0].second, a.W, Gb[0]);
-#define CCE_REC(FILT, CAP)                                                                    \
+      const RecArgs r = with_skip(rec_args(a, 0, chunks[0].second, a.W, Gb[0]), 0, 0);
+#define CCE_REC(FILT, CAP, SK)                                                                \
   CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
-            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
-      if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
-      else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP, SK>), dim3(r.nl), dim3(NT), 0, st, r))
+#define CCE_REC_S(FILT, CAP) \
+  do { if (skip) CCE_REC(FILT, CAP, true); else CCE_REC(FILT, CAP, false); } while (0)
+      if (cap) { if (filt) CCE_REC_S(true, true); else CCE_REC_S(false, true); }
+      else { if (filt) CCE_REC_S(true, false); else CCE_REC_S(false, false); }
+#undef CCE_REC_S
 #undef CCE_REC
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -861,21 +993,32 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       // 384-row dW tiles inside the pipelined launches; the last chunk's
       // contractions run alone, where 256-row dW tiles pack into whole rounds
       // (at 16384 wide: 320 dh tasks of two units and 640 dW tasks of one)
-      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp, c + 1 < nch);
+      grads_probs(a, v0, vlen, a.W + (size_t)v0 * a.D, Gb[c & 1], dh, dw, sp,
+                  c + 1 < nch && !skip);
+      dh.kflags = dw.kflags = Fl[c & 1];
       if (c + 1 < nch) {
         const int v1 = chunks[c + 1].first;
-        const RecArgs r = rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]);
+        const RecArgs r = with_skip(
+            rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]), v1,
+            (c + 1) & 1);
         const dim3 grid(dh.nl + dw.nl + r.nl);
-#define CCE_FUSED(FILT, CAP)                                                                  \
+#define CCE_FUSED(FILT, CAP, SK)                                                              \
   CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * (2.0 * vlen + r.vlen), st,                        \
-            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r))
-        if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
-        else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, SK>), grid, dim3(NT), 0, st, dh, dw, r))
+#define CCE_FUSED_S(FILT, CAP) \
+  do { if (skip) CCE_FUSED(FILT, CAP, true); else CCE_FUSED(FILT, CAP, false); } while (0)
+        if (cap) { if (filt) CCE_FUSED_S(true, true); else CCE_FUSED_S(false, true); }
+        else { if (filt) CCE_FUSED_S(true, false); else CCE_FUSED_S(false, false); }
+#undef CCE_FUSED_S
 #undef CCE_FUSED
       } else {
-        CCE_TIMED(KN_GRADS, 4.0 * a.M * a.D * vlen, st,
-                  hipLaunchKernelGGL((k_grads<false, true>), dim3(dh.nl + dw.nl), dim3(NT), 0, st,
-                                     dh, dw));
+        const dim3 grid(dh.nl + dw.nl);
+        if (skip)
+          CCE_TIMED(KN_GRADS, 4.0 * a.M * a.D * vlen, st,
+                    hipLaunchKernelGGL((k_grads<true, true>), grid, dim3(NT), 0, st, dh, dw));
+        else
+          CCE_TIMED(KN_GRADS, 4.0 * a.M * a.D * vlen, st,
+                    hipLaunchKernelGGL((k_grads<false, true>), grid, dim3(NT), 0, st, dh, dw));
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = split_reduce(dh, sp, st)) != hipSuccess) return e;
@@ -898,7 +1041,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       const RecArgs r = rec_args(a, 0, chunks[0].second, Wb[0], Gb[0]);
 #define CCE_REC(FILT, CAP)                                                                    \
   CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
-            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP, false>), dim3(r.nl), dim3(NT), 0, st, r))
       if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
       else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
 #undef CCE_REC
@@ -918,7 +1061,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
         const dim3 grid(dh.nl + r.nl);
 #define CCE_FUSED(FILT, CAP)                                                                  \
   CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * ((double)vlen + r.vlen), st,                      \
-            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP>), grid, dim3(NT), 0, st, dh, dw, r))
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, false>), grid, dim3(NT), 0, st, dh, dw, r))
         if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
         else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
 #undef CCE_FUSED
@@ -947,7 +1090,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       const RecArgs r = rec_args(a, v0, vlen, Wc, a.G);
 #define CCE_REC(FILT, CAP)                                                                    \
   CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
-            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP>), dim3(r.nl), dim3(NT), 0, st, r))
+            hipLaunchKernelGGL((k_recompute_tall<FILT, CAP, false>), dim3(r.nl), dim3(NT), 0, st, r))
       if (cap) { if (filt) CCE_REC(true, true); else CCE_REC(false, true); }
       else { if (filt) CCE_REC(true, false); else CCE_REC(false, false); }
 #undef CCE_REC

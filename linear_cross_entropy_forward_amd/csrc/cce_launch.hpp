@@ -136,6 +136,7 @@ struct BwdArgs {
   u16* G;      // [Mpad, Vc] bf16, blocked (256 x 32 blocks)
   u16* G2;     // null, or a second such buffer (the pipelined backward)
   int* flags;  // [nMt, Vc / kTile]
+  int* flags2;  // null, or a second such array (the pipelined backward's other gradient buffer)
   unsigned* status;
   // quantised head (q.Wq != null): each chunk is dequantised into Wbuf first,
   // and dW is not formed (the quantised head is frozen; dW may be null)
