@@ -1088,6 +1088,27 @@ __device__ __forceinline__ void sub64(const Dma128& da, const Dma128& db, const 
 // acc = A[0:256, 0:K] . B[0:256, 0:K]^T, both row-major and 16-byte aligned,
 // K % 64 == 0 (rows past A.rows / B.rows read as zero), through the 128 KB ring
 // at `ring`.  Ends with every load drained and a barrier (LDS free).
+// The loads of a 64-wide tile's first K-slice pair, into stage 0 of a ring
+// that no wave still reads: a persistent caller issues them for its next tile
+// right after a tile's K loop, so that they land while it runs that tile's
+// epilogue, and then calls gemm_tile64<false>.
+__device__ __forceinline__ void gemm_tile64_first(const OpRef& A, const OpRef& B,
+                                                  unsigned char* ring) {
+  const int tid = opaque_tid(), lane = tid & 63, w = tid >> 6;
+  unsigned ring_lds = lds_addr(ring);
+  Dma128 da, db;
+  da.init(A, lane, w);
+  db.init(B, lane, w);
+  asm volatile("" : "+s"(ring_lds));
+#pragma unroll
+  for (int p = 0; p < 8; ++p) da.issue(0, ring_lds, p);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) db.issue(0, ring_lds + S64_A, p);
+}
+
+// FIRST: issue the first pair's loads here (else gemm_tile64_first did, and
+// nothing else is in flight but them and stores).
+template <bool FIRST = true>
 __device__ __forceinline__ void gemm_tile64(const OpRef& A, const OpRef& B, int K, unsigned char* ring,
                                             floatx16 (&acc)[4][4]) {
   const int tid = opaque_tid(), lane = tid & 63, w = tid >> 6;
@@ -1100,10 +1121,12 @@ __device__ __forceinline__ void gemm_tile64(const OpRef& A, const OpRef& B, int 
   db.init(B, lane, w);
   asm volatile("" : "+s"(ring_lds));
   const int np = K / 64, klast = (np - 1) * 64;
+  if (FIRST) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) da.issue(0, ring_lds, p);
+    for (int p = 0; p < 8; ++p) da.issue(0, ring_lds, p);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) db.issue(0, ring_lds + S64_A, p);
+    for (int p = 0; p < 8; ++p) db.issue(0, ring_lds + S64_A, p);
+  }
   CCE_WAIT_VMCNT(0);
   ring_barrier();
   Frags f0, f1;

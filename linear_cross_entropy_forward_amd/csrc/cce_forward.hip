@@ -89,6 +89,14 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
     s_run[jj] = 0.f;
   }
   const int t_end = min(t0 + (split + 1) * T, t1);
+  // 64-wide K-slices: each tile's first loads are issued before the previous
+  // tile's epilogue, so they land while it runs
+  const bool k64 = VEC && !KTAIL && (D % 64) == 0;
+  if (k64 && t0 + split * T < t_end) {
+    const int v0 = (t0 + split * T) * TILE;
+    gemm_tile64_first(OpRef{W + (size_t)v0 * D, D, min(TILE, V - v0), D},
+                      OpRef{H + (size_t)mt * TILE * D, D, min(TILE, M - mt * TILE), D}, sm.raw);
+  }
 
   for (int t = t0 + split * T; t < t_end; ++t) {
     // per-tile operand descriptors are rebuilt from scalars every tile (the
@@ -100,10 +108,15 @@ __global__ __launch_bounds__(NT, 1) void k_fwd(const u16* __restrict__ H, const 
     const int hrows = min(TILE, M - mt_ * TILE);
     const int v0 = t * TILE;
     floatx16 acc[4][4];
-    if (VEC && !KTAIL && (D_ % 64) == 0)  // 64-wide K-slices: 128 bytes a row per load
-      gemm_tile64(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_}, OpRef{Hb, D_, hrows, D_},
-                  D_, sm.raw, acc);
-    else
+    if (k64) {  // 64-wide K-slices: 128 bytes a row per load
+      gemm_tile64<false>(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_},
+                         OpRef{Hb, D_, hrows, D_}, D_, sm.raw, acc);
+      if (t + 1 < t_end) {
+        const int v1 = v0 + TILE;
+        gemm_tile64_first(OpRef{W + (size_t)v1 * D_, D_, min(TILE, V - v1), D_},
+                          OpRef{Hb, D_, hrows, D_}, sm.raw);
+      }
+    } else
       gemm_tile<VEC, false, KTAIL>(OpRef{W + (size_t)v0 * D_, D_, min(TILE, V - v0), D_},
                                    OpRef{Hb, D_, hrows, D_}, D_, nullptr, 0, sm, acc);
     if (CAP) {
