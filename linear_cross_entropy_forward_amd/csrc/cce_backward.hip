@@ -372,9 +372,15 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
   if (SKIP && !r.bm) {
     // the largest softmax entry of each block part: tile rows below `split`
     // are in block b_lo, the rest in b_lo + 1 (split is 256 or 128, a multiple
-    // of the 32-row MFMA tiles)
+    // of the 32-row MFMA tiles).  The entry grows with the logit (and the cap is
+    // monotonic), so the largest logit per token and part is taken first and
+    // one exponential per token and part gives the largest entry.
     const int split = (b_lo + 1) * TILE - vt * TALL;
-    float pm[2] = {0.f, 0.f};
+    float zm[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) zm[q][jj] = NEG_INF;
     bool tg[2] = {false, false};
     auto part_max = [&](const floatx16(&t)[4], int row0) {
       const int q = row0 >= split ? 1 : 0;
@@ -382,17 +388,23 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
       for (int r16 = 0; r16 < 16; ++r16) {
         const bool vbad = vt * TALL + row0 + 8 * (r16 >> 2) + 4 * half + (r16 & 3) >= vlen;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float z = CAP ? tanh_scaled(t[jj][r16], k2) : t[jj][r16];
-          const float p = fast_exp2(fmaf(z, c1, nlse[jj]));
-          if (!vbad) pm[q] = fmaxf(pm[q], p);
-        }
+        for (int jj = 0; jj < 4; ++jj)
+          if (!vbad) zm[q][jj] = fmaxf(zm[q][jj], t[jj][r16]);
       }
     };
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) part_max(acc.a[ii], wi * 192 + ii * 32);
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) part_max(acc.v[ii], wi * 192 + 128 + ii * 32);
+    float pm[2] = {0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if (zm[q][jj] == NEG_INF) continue;
+        const float z = CAP ? tanh_scaled(zm[q][jj], k2) : zm[q][jj];
+        pm[q] = fmaxf(pm[q], fast_exp2(fmaf(z, c1, nlse[jj])));
+      }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
