@@ -40,6 +40,7 @@ struct Layout {
   size_t part_m, part_s, tgt, pairs, g, flags, flags2;
   size_t epi_rec, epi_nruns, epi_first, epi_last, epi_end;  // the epilogue's row-pass state
   size_t tc, skey[2], sval[2], shist, tF, tL;  // the backward's exact onehot part
+  size_t queue;  // the pipelined backward's task-queue counters
   size_t g2;  // the second gradient buffer of the pipelined backward (0: none)
   size_t psplit;  // split-K partial tiles of dh (psplit_tiles of 256 x 256 fp32)
   long long psplit_tiles;
@@ -96,6 +97,7 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.shist = take((size_t)256 * ((M + 2047) / 2048) * sizeof(int));
   L.tF = take((size_t)((M + 63) / 64) * D * sizeof(float));
   L.tL = take((size_t)((M + 63) / 64) * D * sizeof(float));
+  L.queue = take((size_t)cce::kQueueInts * sizeof(int));
   L.g = take((size_t)L.Mpad * L.Vc * 2);
   L.flags = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
   L.flags2 = take((size_t)L.nMt * (L.Vc / kTile) * sizeof(int));
@@ -151,6 +153,7 @@ void set_target_regions(cce::BwdArgs& a, const Layout& L, char* base) {
   a.shist = reinterpret_cast<int*>(base + L.shist);
   a.tF = reinterpret_cast<float*>(base + L.tF);
   a.tL = reinterpret_cast<float*>(base + L.tL);
+  a.queue = reinterpret_cast<int*>(base + L.queue);
 }
 
 // Scratch of the no-allocation forward (cce_forward_noalloc): one array per

@@ -263,7 +263,37 @@ struct RecArgs {
   int* flags;
   const float* bm;
   float block_eps;
+  int* qzero;  // null, or a set of task-queue counters that workgroup 0 clears
 };
+
+// Task queues of the pipelined launches' recompute tiles: per launch one set
+// of 8 counters (one per XCD, 64 bytes apart); launch c takes set c % 2 and
+// clears the other for launch c + 1 (the launch before it used that set and
+// has finished; the first launch's set is cleared by the recompute launch
+// before it).
+constexpr int kQueueStride = 16;
+constexpr int kQueueSet = 8 * kQueueStride;
+static_assert(2 * kQueueSet == kQueueInts, "two queue sets fill the counters");
+
+__device__ __forceinline__ void clear_queue_set(int* set) {
+  if (set && blockIdx.x == 0 && threadIdx.x < kQueueSet) set[threadIdx.x] = 0;
+}
+
+__device__ __forceinline__ int queue_len(int n, int x) { return (n - x + 7) >> 3; }
+
+// A ticket from another XCD's queue once the own one is exhausted (-1: none
+// left anywhere).
+__device__ __forceinline__ int steal_task(int* queue, int home, int n) {
+  for (int d = 1; d < 8; ++d) {
+    const int x = (home + d) & 7;
+    int* const c = queue + x * kQueueStride;
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= queue_len(n, x))
+      continue;
+    const int k = atomicAdd(c, 1);
+    if (k < queue_len(n, x)) return x + 8 * k;
+  }
+  return -1;
+}
 
 // Whether v holds for any thread of the workgroup, through 16 bytes of LDS at
 // `scratch` (the operand ring, which must not be in use: the tall tile's 160
@@ -443,6 +473,7 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
 template <bool FILTER, bool CAP, bool SKIP>
 __global__ __launch_bounds__(NT, 1) void k_recompute_tall(RecArgs r) {
   __shared__ SmemTall sm;
+  clear_queue_set(r.qzero);
   recompute_tall_tile<FILTER, CAP, SKIP>(r, blockIdx.x, sm);
 }
 
@@ -775,12 +806,43 @@ __global__ __launch_bounds__(NT, 1) void k_grads(GemmProb p0, GemmProb p1) {
 // overlap other workgroups' contractions.
 // SKIP: the block skip (256-row dW tiles and the compacted K loops of the
 // contractions read the flags the previous launch's recompute tiles wrote).
+//
+// The recompute tiles are taken by at most one workgroup per CU, each looping
+// over tiles until none is left: tile t belongs to queue t % 8 (the XCD a
+// one-tile-per-workgroup launch gives it, keeping the grouped raster's operand
+// sharing inside one L2), and a queue hands its tiles out in order.  A worker
+// takes from its own XCD's queue (workgroup g runs on XCD g % 8), then from
+// the others: the XCDs that finish their share of the launch early take over
+// the rest instead of idling through its tail.  Tiles are independent, every
+// ticket is taken once by an atomic increment of a counter that only grows,
+// and a worker leaves when all 8 queues are exhausted.
 template <bool FILTER, bool CAP, bool SKIP>
-__global__ __launch_bounds__(NT, 1) void k_bwd_fused(GemmProb p0, GemmProb p1, RecArgs r) {
+__global__ __launch_bounds__(NT, 1) void k_bwd_fused(GemmProb p0, GemmProb p1, RecArgs r,
+                                                     int* queue) {
   __shared__ SmemTall sm;
+  clear_queue_set(r.qzero);
   const int b = blockIdx.x, ng = p0.nl + p1.nl;
-  if (b < ng) grads_task<SKIP, true>(p0, p1, b, sm);
-  else recompute_tall_tile<FILTER, CAP, SKIP>(r, b - ng, sm);
+  if (b < ng) {
+    grads_task<SKIP, true>(p0, p1, b, sm);
+    return;
+  }
+  const int home = b & 7;
+  int* const own = queue + home * kQueueStride;
+  volatile int* const slot = reinterpret_cast<volatile int*>(sm.raw);
+  for (;;) {
+    // the ring is free here (a tile ends with its loads drained and a
+    // barrier; the loop's last barrier follows it)
+    if (threadIdx.x == 0) {
+      const int k = atomicAdd(own, 1);
+      *slot = k < queue_len(r.nl, home) ? home + 8 * k : steal_task(queue, home, r.nl);
+    }
+    __syncthreads();
+    const int t = *slot;
+    __syncthreads();
+    if (t < 0) break;
+    recompute_tall_tile<FILTER, CAP, SKIP>(r, t, sm);
+    __syncthreads();
+  }
 }
 
 static inline int pad8(int n) { return (n + 7) / 8 * 8; }
@@ -927,7 +989,8 @@ static RecArgs rec_args(const BwdArgs& a, int v0, int vlen, const u16* Wc, u16* 
   const int nvt3 = (vlen + TALL - 1) / TALL;
   return RecArgs{a.H,     Wc,           a.y, a.lse, a.coef, a.M, a.D,        v0,
                  vlen,    a.nMt,        nvt3, a.softcap, a.filter_eps, G, a.Vc / 32,
-                 (vlen + kTile - 1) / kTile * 8, pad8(a.nMt * nvt3), nullptr, nullptr, 0.f};
+                 (vlen + kTile - 1) / kTile * 8, pad8(a.nMt * nvt3), nullptr, nullptr, 0.f,
+                 nullptr};
 }
 
 static hipError_t split_reduce(const GemmProb& dh, const DhSplit& sp, hipStream_t st) {
@@ -986,7 +1049,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       return r;
     };
     {
-      const RecArgs r = with_skip(rec_args(a, 0, chunks[0].second, a.W, Gb[0]), 0, 0);
+      RecArgs r = with_skip(rec_args(a, 0, chunks[0].second, a.W, Gb[0]), 0, 0);
+      r.qzero = a.queue;  // the first fused launch's queue set
 #define CCE_REC(FILT, CAP, SK)                                                                \
   CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
             hipLaunchKernelGGL((k_recompute_tall<FILT, CAP, SK>), dim3(r.nl), dim3(NT), 0, st, r))
@@ -1010,13 +1074,16 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       dh.kflags = dw.kflags = Fl[c & 1];
       if (c + 1 < nch) {
         const int v1 = chunks[c + 1].first;
-        const RecArgs r = with_skip(
+        RecArgs r = with_skip(
             rec_args(a, v1, chunks[c + 1].second, a.W + (size_t)v1 * a.D, Gb[(c + 1) & 1]), v1,
             (c + 1) & 1);
-        const dim3 grid(dh.nl + dw.nl + r.nl);
+        int* const qset = a.queue + (c & 1) * kQueueSet;
+        r.qzero = a.queue + ((c + 1) & 1) * kQueueSet;
+        const dim3 grid(dh.nl + dw.nl + (r.nl < kCUs ? r.nl : kCUs));
 #define CCE_FUSED(FILT, CAP, SK)                                                              \
   CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * (2.0 * vlen + r.vlen), st,                        \
-            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, SK>), grid, dim3(NT), 0, st, dh, dw, r))
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, SK>), grid, dim3(NT), 0, st, dh, dw, r, \
+                               qset))
 #define CCE_FUSED_S(FILT, CAP) \
   do { if (skip) CCE_FUSED(FILT, CAP, true); else CCE_FUSED(FILT, CAP, false); } while (0)
         if (cap) { if (filt) CCE_FUSED_S(true, true); else CCE_FUSED_S(false, true); }
@@ -1050,7 +1117,8 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
     u16* const Wb[2] = {a.Wbuf, a.Wbuf2};
     if ((e = launch_dequant(a.q, 0, chunks[0].second, a.D, Wb[0], st)) != hipSuccess) return e;
     {
-      const RecArgs r = rec_args(a, 0, chunks[0].second, Wb[0], Gb[0]);
+      RecArgs r = rec_args(a, 0, chunks[0].second, Wb[0], Gb[0]);
+      r.qzero = a.queue;
 #define CCE_REC(FILT, CAP)                                                                    \
   CCE_TIMED(KN_RECOMPUTE_TALL, 2.0 * a.M * a.D * r.vlen, st,                                  \
             hipLaunchKernelGGL((k_recompute_tall<FILT, CAP, false>), dim3(r.nl), dim3(NT), 0, st, r))
@@ -1068,12 +1136,15 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
       if (!last) {
         const int v1 = chunks[c + 1].first, vlen1 = chunks[c + 1].second;
         if ((e = launch_dequant(a.q, v1, vlen1, a.D, Wb[(c + 1) & 1], st)) != hipSuccess) return e;
-        const RecArgs r = rec_args(a, v1, vlen1, Wb[(c + 1) & 1], Gb[(c + 1) & 1]);
+        RecArgs r = rec_args(a, v1, vlen1, Wb[(c + 1) & 1], Gb[(c + 1) & 1]);
+        int* const qset = a.queue + (c & 1) * kQueueSet;
+        r.qzero = a.queue + ((c + 1) & 1) * kQueueSet;
         dw.nl = 0;  // dh tasks only
-        const dim3 grid(dh.nl + r.nl);
+        const dim3 grid(dh.nl + (r.nl < kCUs ? r.nl : kCUs));
 #define CCE_FUSED(FILT, CAP)                                                                  \
   CCE_TIMED(KN_BWD_FUSED, 2.0 * a.M * a.D * ((double)vlen + r.vlen), st,                      \
-            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, false>), grid, dim3(NT), 0, st, dh, dw, r))
+            hipLaunchKernelGGL((k_bwd_fused<FILT, CAP, false>), grid, dim3(NT), 0, st, dh, dw, r, \
+                               qset))
         if (cap) { if (filt) CCE_FUSED(true, true); else CCE_FUSED(false, true); }
         else { if (filt) CCE_FUSED(true, false); else CCE_FUSED(false, false); }
 #undef CCE_FUSED

@@ -157,7 +157,9 @@ struct BwdArgs {
   int* shist;
   float* tF;  // [ceil(M / 64), D]: per window of the sorted rows, a run's first / last piece
   float* tL;
+  int* queue;  // kQueueInts: the recompute task queues of the pipelined launches
 };
+constexpr int kQueueInts = 256;  // two sets of 8 counters, 64 bytes apart
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 // dh = -t_i W_{y_i} for every row (before the chunks accumulate into it), and
 // t / the sort input; then, after the chunks wrote dW, dW_v -= sum t_i h_i over
