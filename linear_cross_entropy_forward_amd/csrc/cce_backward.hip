@@ -52,19 +52,31 @@ namespace cce {
 // the first nblk of them are stored (the blocks the dh contraction reads).
 // RAW (with CAP): acc holds the raw logits z and t = tanh(z / c) is formed here
 // (k2 = 2 log2(e) / c), so no pass rewrites the accumulators beforehand.
-template <bool CAP, bool FILTER, bool TGT, bool VT, int NI = 4, bool RAW = false>
+// LIVE: the pass also notes, per lane, whether some softmax entry it forms is
+// >= lv->eps, separately for the two block parts of a tall tile: rows
+// [0, lv->split) of this call's range lie in the first block, the rest in the
+// second (split is a multiple of 32, so the part is fixed per ii).
+struct PartLive {
+  float eps;
+  int split;
+  bool l0, l1;
+};
+
+template <bool CAP, bool FILTER, bool TGT, bool VT, int NI = 4, bool RAW = false,
+          bool LIVE = false>
 __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
                                                 const float (&nlse)[4], const float (&cf)[4],
                                                 const int (&off)[4], float c1, float filter_eps,
                                                 int vl0, int vlen, int half, int wj, int lane,
                                                 u16* __restrict__ gt, int nblk = NI,
-                                                float k2 = 0.f) {
+                                                float k2 = 0.f, PartLive* lv = nullptr) {
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int tj = wj * 128 + jj * 32 + (lane & 31);
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
       if (ii >= nblk) continue;
+      const bool in1 = LIVE && ii * 32 >= lv->split;
       unsigned pk[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -80,6 +92,11 @@ __device__ __forceinline__ void store_grad_tile(const floatx16 (&acc)[NI][4],
           } else {
             p = fast_exp2(fmaf(acc[ii][jj][4 * q + e], LOG2E, nlse[jj]));
             if (vbad) p = 0.f;
+          }
+          if (LIVE) {
+            const bool hit = p >= lv->eps;
+            lv->l0 |= hit && !in1;
+            lv->l1 |= hit && in1;
           }
           // the target's entry is kept from the filter; its onehot part (-coef
           // sech^2) is applied outside these tiles, exactly
@@ -334,10 +351,11 @@ __device__ __forceinline__ void put_block_flag(int* flags, int fstride, int mt, 
 // whole).  With the saved block maximum the test comes first: each block's
 // liveness is decided from it (exp(bm - lse) >= block_eps for some token, or a
 // token's target in the block), and a tile whose blocks are both dead is not
-// recomputed at all.  Without it the tile is recomputed, its largest softmax
-// entry taken per block part, and the parts' votes combine in the block's flag
-// (put_block_flag); the tile's gradient entries are stored either way, and the
-// contractions leave out the dead blocks.
+// recomputed at all.  Without it the tile is recomputed, the store pass notes
+// per block part whether some softmax entry reaches block_eps, and the parts'
+// votes combine in the block's flag (put_block_flag); the tile's gradient
+// entries are stored either way, and the contractions leave out the dead
+// blocks.
 template <bool FILTER, bool CAP, bool SKIP = false>
 __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, SmemTall& sm) {
   const u16* __restrict__ H = r.H;
@@ -399,42 +417,36 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
   const float c1 = CAP ? softcap * LOG2E : LOG2E;  // log2 of the softmax numerator per unit
   const float k2 = CAP ? 2.f * LOG2E / softcap : 0.f;  // the cap's tanh is taken at the store
   const bool vtail = vt * TALL + TALL > vlen;
+  // SKIP without the saved maximum: the store pass notes, per block part,
+  // whether some softmax entry is >= block_eps (tile rows below `split` are in
+  // block b_lo, the rest in b_lo + 1; split is 256 or 128, a multiple of the
+  // 32-row MFMA tiles); the parts' votes and the targets then set the flags.
+  constexpr bool LIVE = SKIP;
+  const int split = (b_lo + 1) * TILE - vt * TALL;
+  PartLive la{r.block_eps, split - wi * 192, false, false};
+  PartLive lv{r.block_eps, split - wi * 192 - 128, false, false};
+  const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
+  const int b0 = vt * 12 + wi * 6;  // this wave's first vocab block of the chunk
+  const int nb = min(max(nkb - b0, 0), 6);
+  u16* gt = G + ((size_t)mt * nkbV + b0) * 8192;
+#define CCE_STORE(TGT, VT)                                                                     \
+  do {                                                                                         \
+    store_grad_tile<CAP, FILTER, TGT, VT, 4, true, LIVE>(acc.a, nlse, cf, off, c1, filter_eps, \
+                                                         vl0, vlen, half, wj, lane, gt,        \
+                                                         min(nb, 4), k2, &la);                 \
+    store_grad_tile<CAP, FILTER, TGT, VT, 2, true, LIVE>(acc.v, nlse, cf, off2, c1,            \
+                                                         filter_eps, vl0 + 128, vlen, half,    \
+                                                         wj, lane, gt + 4 * 8192, nb - 4, k2,  \
+                                                         &lv);                                 \
+  } while (0)
+  if (wave_has_tgt) {
+    if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
+  } else {
+    if (vtail) CCE_STORE(false, true); else CCE_STORE(false, false);
+  }
+#undef CCE_STORE
   if (SKIP && !r.bm) {
-    // the largest softmax entry of each block part: tile rows below `split`
-    // are in block b_lo, the rest in b_lo + 1 (split is 256 or 128, a multiple
-    // of the 32-row MFMA tiles).  The entry grows with the logit (and the cap is
-    // monotonic), so the largest logit per token and part is taken first and
-    // one exponential per token and part gives the largest entry.
-    const int split = (b_lo + 1) * TILE - vt * TALL;
-    float zm[2][4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) zm[q][jj] = NEG_INF;
     bool tg[2] = {false, false};
-    auto part_max = [&](const floatx16(&t)[4], int row0) {
-      const int q = row0 >= split ? 1 : 0;
-#pragma unroll
-      for (int r16 = 0; r16 < 16; ++r16) {
-        const bool vbad = vt * TALL + row0 + 8 * (r16 >> 2) + 4 * half + (r16 & 3) >= vlen;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (!vbad) zm[q][jj] = fmaxf(zm[q][jj], t[jj][r16]);
-      }
-    };
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) part_max(acc.a[ii], wi * 192 + ii * 32);
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) part_max(acc.v[ii], wi * 192 + 128 + ii * 32);
-    float pm[2] = {0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (zm[q][jj] == NEG_INF) continue;
-        const float z = CAP ? tanh_scaled(zm[q][jj], k2) : zm[q][jj];
-        pm[q] = fmaxf(pm[q], fast_exp2(fmaf(z, c1, nlse[jj])));
-      }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = mt * TILE + wj * 128 + jj * 32 + (lane & 31);
@@ -443,31 +455,13 @@ __device__ __forceinline__ void recompute_tall_tile(const RecArgs& r, int b, Sme
       tg[0] |= (unsigned)o < (unsigned)TILE;
       tg[1] |= (unsigned)(o - TILE) < (unsigned)TILE;
     }
-    const bool live0 = block_any(pm[0] >= r.block_eps || tg[0], sm.raw);
-    const bool live1 = block_any(pm[1] >= r.block_eps || tg[1], sm.raw);
+    const bool live0 = block_any(la.l0 || lv.l0 || tg[0], sm.raw);
+    const bool live1 = block_any(la.l1 || lv.l1 || tg[1], sm.raw);
     if (tid == 0) {
       put_block_flag(r.flags, fstride, mt, b_lo, vt, r.nvt, live0);
       if (two) put_block_flag(r.flags, fstride, mt, b_lo + 1, vt, r.nvt, live1);
     }
   }
-  const bool wave_has_tgt = __ballot(any_tgt_lane) != 0ull;
-  const int b0 = vt * 12 + wi * 6;  // this wave's first vocab block of the chunk
-  const int nb = min(max(nkb - b0, 0), 6);
-  u16* gt = G + ((size_t)mt * nkbV + b0) * 8192;
-#define CCE_STORE(TGT, VT)                                                                     \
-  do {                                                                                         \
-    store_grad_tile<CAP, FILTER, TGT, VT, 4, true>(acc.a, nlse, cf, off, c1, filter_eps, vl0,  \
-                                                   vlen, half, wj, lane, gt, min(nb, 4), k2);  \
-    store_grad_tile<CAP, FILTER, TGT, VT, 2, true>(acc.v, nlse, cf, off2, c1, filter_eps,      \
-                                                   vl0 + 128, vlen, half, wj, lane,            \
-                                                   gt + 4 * 8192, nb - 4, k2);                 \
-  } while (0)
-  if (wave_has_tgt) {
-    if (vtail) CCE_STORE(true, true); else CCE_STORE(true, false);
-  } else {
-    if (vtail) CCE_STORE(false, true); else CCE_STORE(false, false);
-  }
-#undef CCE_STORE
 }
 
 template <bool FILTER, bool CAP, bool SKIP>
