@@ -215,15 +215,20 @@ cce_status cce_backward(const void* h, const void* W, const int32_t* y,
  * cce_backward on the bf16-rounded dequantised head.
  */
 
-/* Workspace bytes for cce_forward_q / cce_backward_q: cce_workspace_bytes
- * without its second gradient buffer (the quantised backward is not
- * pipelined), plus one bf16 chunk of the dequantised head (16384 x D) and two
- * [M] fp32 rows; independent of V above one chunk.  0 for invalid sizes.
- * Host-only. */
+/* Workspace bytes for cce_forward_q / cce_backward_q: the parts of
+ * cce_workspace_bytes the two calls share (forward partials, epilogue state,
+ * exact onehot buffers, the first gradient buffer and its flags), then two
+ * [M] fp32 rows, two bf16 chunks of the dequantised head (16384 x D each) with
+ * a second gradient buffer between them when D % 32 == 0 (the pipelined
+ * backward alternates between the two of each), and the dh split partials;
+ * independent of V above one chunk.  0 for invalid sizes.  Host-only. */
 size_t cce_workspace_bytes_q(int64_t M, int64_t V, int64_t D);
 
-/* Forward over the quantised head; outputs as for cce_forward.  The running
- * (max, sum-exp) of each row is folded chunk by chunk in a fixed order. */
+/* Forward over the quantised head; outputs as for cce_forward.  The head is
+ * dequantised chunk by chunk into the chunk and gradient buffers of the
+ * workspace (the backward's, free during the forward): as few equal chunks of
+ * whole 256-row tiles as that space holds.  The running (max, sum-exp) of each
+ * row is folded chunk by chunk in a fixed order. */
 cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales,
                          const void* biases, int bits, int group_size,
                          const int32_t* y, int64_t M, int64_t V, int64_t D, float softcap,

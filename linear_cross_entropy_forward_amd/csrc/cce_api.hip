@@ -51,6 +51,7 @@ struct Layout {
   size_t g2q, wbuf2;  // the pipelined quantised backward's second G and chunk buffers (0: none)
   long long psplit_tiles_q;
   size_t total_q;
+  int64_t vcf;  // rows of the quantised forward's dequantised chunk
 };
 
 // dh split-K partial tiles reserved for a full vocab chunk: as many as its
@@ -119,6 +120,18 @@ Layout layout(int64_t M, int64_t V, int64_t D) {
   L.psplit_tiles_q = split_tiles(L, false);
   L.psplit_q = take((size_t)L.psplit_tiles_q * kTile * kTile * 4);
   L.total_q = off;
+  // the quantised forward dequantises into the chunk and gradient buffers that
+  // follow one another from wbuf (the backward's, free during the forward):
+  // as few equal chunks of whole 256-row tiles as that region holds, so each
+  // launch runs many vocab tiles per workgroup
+  {
+    const size_t row = (size_t)D * 2;
+    const size_t region = (L.wbuf2 ? L.wbuf2 : L.wbuf) + (size_t)L.Vc * row - L.wbuf;
+    const int64_t cap_rows = std::max<int64_t>(L.Vc, (int64_t)(region / row) / kTile * kTile);
+    const int64_t Vpad = round_up(V, kTile);
+    const int64_t nch = (Vpad + cap_rows - 1) / cap_rows;
+    L.vcf = round_up((Vpad + nch - 1) / nch, kTile);
+  }
   return L;
 }
 
@@ -521,7 +534,7 @@ cce_status cce_forward_q(const void* h, const uint32_t* Wq, const void* scales, 
   a.f.bm = block_max;
   a.q = cce::QuantW{reinterpret_cast<const unsigned*>(Wq), static_cast<const cce::u16*>(scales),
                     static_cast<const cce::u16*>(biases), bits, group_size};
-  a.Vc = (int)L.Vc;
+  a.Vc = (int)L.vcf;
   a.Wbuf = reinterpret_cast<cce::u16*>(base + L.wbuf);
   a.run_m = reinterpret_cast<float*>(base + L.run_m);
   a.run_s = reinterpret_cast<float*>(base + L.run_s);

@@ -75,6 +75,7 @@ QUANT = [
     ([(5, 30, 30, 5)], 384, 1000, 4, 128, 30.0, 0.0),                  # softcap, one ragged chunk
     ([(7, 60, 50, 3)], 128, 16384 + 256, 8, 64, 0.0, 1e-6),            # filter; chunk + 1 tile
     ([(0, 1, 1)], 32, 1, 4, 32, 0.0, 0.0),                             # V = 1, M = 2
+    ([(7, 30, 20, 3)], 32, 170001, 4, 32, 0.0, 0.0),                   # forward in 2 chunks, ragged
 ]
 
 
