@@ -346,6 +346,42 @@ def test_block_skip_past_64_token_blocks(device):
     assert np.all(g["dW"][256:512] == 0.0)
 
 
+def test_block_skip_block_live_in_one_half(device):
+    """A 256-entry vocab block that a 384-row recompute tile boundary cuts in
+    two (block 1: rows 256..383 in the first tall tile, 384..511 in the
+    second), live for token block 0 through its upper half only: the block's
+    flag combines both tiles' votes, so it must stay live there (its entries
+    reach the gradient) and be skipped for the other token blocks; against the
+    oracle's block-skip gradient."""
+    spans = [(100, 300, 290, 30)]
+    wl = WL.make_custom(spans, D=64, V=1024, seed=9, hidden_scale=1.0, w_std=0.05, lam=0.2)
+    Hf = WL.bf16_bits_to_f32(wl.h_bits).copy()
+    Hf[:, 0] = 4.0
+    Wf = WL.bf16_bits_to_f32(wl.W_bits).copy()
+    Wf[256:512, 0] = -4.0            # block 1 near -16 on every row
+    Hf[0:256, 1] = 8.0
+    Wf[400:512, 1] = 1.5             # ... lifted to about -4 for token block 0, upper half only
+    wl.h_bits = WL.f32_to_bf16_bits(Hf)
+    wl.W_bits = WL.f32_to_bf16_bits(Wf)
+    wl.y = np.where((wl.y >= 256) & (wl.y < 512), wl.y % 256, wl.y).astype(np.int32)
+    eps = 1e-6
+    say(f"[gpu] block skip, block live in one half: M={wl.M} V={wl.V} D={wl.D}")
+    g, st = run_gpu(wl, device, filter_eps=eps, block_eps=eps)
+    assert st == 0
+    H, W = wl.h64(), wl.W64()
+    o = O.step(H, W, wl.y, wl.seg, 1, wl.lam, wl.scope)
+    dead = O.dead_blocks(O.block_max(H, W), o["lse"], wl.y, eps)
+    assert not dead[0, 1] and dead[1:, 1].all()
+    dh_f, dW_f = O.backward(H, W, wl.y, o["lse"], o["coef"], filter_eps=eps, block_eps=eps)
+    e_dh, e_dW = rel_l2(g["dh"], dh_f), rel_l2(g["dW"], dW_f)
+    e_half = rel_l2(g["dW"][400:512], dW_f[400:512])
+    say(f"  vs the oracle's block-skip gradient: dh {e_dh:.3e} dW {e_dW:.3e} "
+        f"(rows 400..511: {e_half:.3e})")
+    assert e_dh <= RTOL_GRAD and e_dW <= RTOL_GRAD and e_half <= RTOL_GRAD
+    assert np.abs(dW_f[400:512]).max() > 0.0
+    assert np.all(g["dW"][256:400] == 0.0)           # filtered or skipped everywhere
+
+
 def test_block_skip_matches_filtered_oracle(device):
     """A vocab tile whose logits are far below the others is skipped; the result
     equals the oracle's filtered gradient at the same eps."""
