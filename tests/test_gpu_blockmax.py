@@ -143,12 +143,15 @@ def test_backward_skip_from_block_max(device, case):
         assert np.all(dW_b[b * 256:(b + 1) * 256] == 0.0)
 
 
-def test_quant_head_block_max(device):
+@pytest.mark.parametrize("D,V", [(128, 17000), (64, 170001)])
+def test_quant_head_block_max(device, D, V):
     """The quantised head's forward writes the same block maximum as the bf16
     head on its dequantised values, and its dh with the stored skip equals the
     bf16 backward's up to the order of fp32 sums (its dh may split K
-    differently: the frozen head has no dW)."""
-    spans, D, V = [(10, 200, 190, 16)], 128, 17000
+    differently: the frozen head has no dW).  At V = 170001, D = 64 the
+    quantised forward runs in two chunks, the second ragged, each writing its
+    part of the block maximum."""
+    spans = [(10, 200, 190, 16)]
     wl = WL.make_custom(spans, D=D, V=V, seed=700, w_std=0.05)
     dead_structure(wl, np.arange(1024, 1536), sink=-3.0)
     qh = WL.quantize_affine(WL.bf16_bits_to_f32(wl.W_bits), 8, 64)
