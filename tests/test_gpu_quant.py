@@ -76,6 +76,7 @@ QUANT = [
     ([(7, 60, 50, 3)], 128, 16384 + 256, 8, 64, 0.0, 1e-6),            # filter; chunk + 1 tile
     ([(0, 1, 1)], 32, 1, 4, 32, 0.0, 0.0),                             # V = 1, M = 2
     ([(7, 30, 20, 3)], 32, 170001, 4, 32, 0.0, 0.0),                   # forward in 2 chunks, ragged
+    ([(7, 30, 20, 3)], 64, 170001, 8, 64, 20.0, 1e-6),                 # the same with cap and filter
 ]
 
 
