@@ -445,6 +445,22 @@ def test_run_to_run_bytes_identical(device):
         assert a[k].tobytes() == b[k].tobytes(), k
 
 
+@pytest.mark.parametrize("eps", [0.0, 1e-5])
+def test_run_to_run_bytes_identical_work_queue(device, eps):
+    """8192 rows (32 token tiles) over three vocab chunks: each pipelined
+    launch hands 1280 recompute tiles to at most 256 workers through the
+    per-XCD queues, so which workgroup computes which tile changes from run to
+    run (stealing included); every output is still byte-identical, with and
+    without the filter and block skip."""
+    wl = WL.make_custom([(1000, 3600, 3500, 92)], D=64, V=40000, seed=6, targets="zipf",
+                        hidden_scale=3.0)
+    assert wl.M == 8192
+    a, _ = run_gpu(wl, device, filter_eps=eps, block_eps=eps)
+    b, _ = run_gpu(wl, device, filter_eps=eps, block_eps=eps)
+    for k in ("logp", "lse", "out5", "coef", "dh", "dW"):
+        assert a[k].tobytes() == b[k].tobytes(), k
+
+
 # ----------------------------------------------------------------------------
 # full-size configs in the benchmark's launch configuration: the oracle's
 # forward and epilogue over every row (seconds to a minute of fp64 on the host
