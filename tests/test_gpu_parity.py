@@ -461,6 +461,40 @@ def test_run_to_run_bytes_identical_work_queue(device, eps):
         assert a[k].tobytes() == b[k].tobytes(), k
 
 
+def test_workspace_reuse_leaves_nothing_behind(device):
+    """One head (one workspace) runs a step on one input and then on another:
+    the second step's outputs are byte-identical to a fresh head's on that
+    input (gradient buffers, block flags and work-queue counters are all
+    rewritten or cleared by the step that uses them), with the block skip on
+    and a first input whose vocab rows 10000..19999 are dead for every row."""
+    eps = 1e-5
+    wa = WL.make_custom([(1000, 3600, 3500, 92)], D=64, V=40000, seed=11, targets="zipf")
+    wb = WL.make_custom([(1000, 3600, 3500, 92)], D=64, V=40000, seed=12, targets="zipf")
+    # the first input: vocab rows 10000..19999 sink to about -16 on every row
+    Hf = WL.bf16_bits_to_f32(wa.h_bits).copy()
+    Hf[:, 0] = 4.0
+    Wf = WL.bf16_bits_to_f32(wa.W_bits).copy()
+    Wf[10000:20000, 0] = -4.0
+    wa.h_bits = WL.f32_to_bf16_bits(Hf)
+    wa.W_bits = WL.f32_to_bf16_bits(Wf)
+    wa.y = np.where((wa.y >= 10000) & (wa.y < 20000), wa.y - 10000, wa.y).astype(np.int32)
+    head = B.Head(wa.M, wa.V, wa.D, device)
+    outs = []
+    for wl in (wa, wb):
+        h, W, y, seg = upload(wl, device)
+        head.clear_status()
+        out = B.step(head, h, W, y, seg, wl.n_pairs, wl.lam, wl.scope, eps, eps)
+        torch.cuda.synchronize()
+        assert head.read_status() == 0
+        outs.append({k: v.detach().cpu().numpy() for k, v in out.items()})
+    del head
+    torch.cuda.empty_cache()
+    fresh, st = run_gpu(wb, device, filter_eps=eps, block_eps=eps)
+    assert st == 0
+    for k in ("logp", "lse", "out5", "coef", "dh", "dW"):
+        assert outs[1][k].tobytes() == fresh[k].tobytes(), k
+
+
 # ----------------------------------------------------------------------------
 # full-size configs in the benchmark's launch configuration: the oracle's
 # forward and epilogue over every row (seconds to a minute of fp64 on the host
