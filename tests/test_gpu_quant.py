@@ -192,3 +192,33 @@ def test_quant_gemma_head_sampled(device):
     e = rel_l2(dh_g[nz], dh_o[nz])
     say(f"  sampled dh rel L2 {e:.3e}")
     assert e <= RTOL_GRAD
+
+
+def test_quant_workspace_reuse(device):
+    """The quantised forward dequantises into the backward's buffers: one head
+    (one workspace) running forward and backward on one head and input, then
+    on another, gives byte-identical results on the second to a fresh
+    head's.  Two forward chunks and more than ten backward chunks."""
+    D, V, bits, group = 64, 170001, 4, 32
+    spans = [(7, 30, 20, 3)]
+
+    def run(head, seed):
+        wl = WL.make_custom(spans, D=D, V=V, seed=seed, w_std=0.05, targets="zipf")
+        qh = WL.quantize_affine(WL.bf16_bits_to_f32(wl.W_bits), bits, group)
+        h = B.to_device_bits(wl.h_bits, device)
+        y = torch.from_numpy(wl.y).to(device)
+        Wq, s, b = quant_upload(qh, device)
+        head.clear_status()
+        logp, lse = head.forward_q(h, Wq, s, b, bits, group, y)
+        coef = torch.from_numpy(seeded_coef(wl, seed + 1)).to(device)
+        dh = head.backward_q(h, Wq, s, b, bits, group, y, lse, coef)
+        torch.cuda.synchronize()
+        assert head.read_status() == 0
+        return [t.cpu().numpy().tobytes() for t in (logp, lse, dh)]
+
+    M = sum(sum(sp) for sp in spans)
+    shared = B.Head(M, V, D, device, quantized=True)
+    run(shared, 900)
+    second = run(shared, 901)
+    fresh = run(B.Head(M, V, D, device, quantized=True), 901)
+    assert second == fresh
