@@ -91,3 +91,24 @@ def test_quant_step_in_graph(device):
     head.clear_status()
     _capture_and_replay(step)
     assert head.read_status() == 0
+
+
+def test_bf16_step_in_graph_work_queues(device):
+    """8192 rows over three vocab chunks, without the skip: two pipelined
+    launches take their recompute tiles from the two alternating sets of
+    work-queue counters, which the launches themselves clear (no memset node
+    in the graph); every replay matches the eager step byte for byte."""
+    wl = WL.make_custom([(1000, 3600, 3500, 92)], D=64, V=40000, seed=902, targets="zipf")
+    say(f"[gpu] graph capture, work queues: M={wl.M} V={wl.V} D={wl.D}")
+    head = B.Head(wl.M, wl.V, wl.D, device)
+    h = B.to_device_bits(wl.h_bits, device)
+    W = B.to_device_bits(wl.W_bits, device)
+    y = torch.from_numpy(wl.y).to(device)
+    seg = torch.from_numpy(wl.seg).to(device)
+
+    def step():
+        return B.step(head, h, W, y, seg, wl.n_pairs, wl.lam, wl.scope)
+
+    head.clear_status()
+    _capture_and_replay(step)
+    assert head.read_status() == 0
